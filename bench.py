@@ -1,0 +1,260 @@
+"""Throughput of the Fast-dLLM block-cache decode path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A "step" of this benchmark is one whole generation (``dllm_generate``): prefill, every
+cached denoising step with its confidence/unmask pass, and the refresh after each block,
+for one batch of seeded synthetic prompts.  Weights, tokens, KV cache and workspace are
+resident in HBM before the timed region.  The default workload is the LLaDA-8B-shaped
+random-init model with DualCache: prompt 1000 tokens, 1024 generated in blocks of 32,
+threshold 0.9, batch 1.
+
+Prints one JSON line: generated tokens/s plus the roofline of the dominant kernel class
+(timed live with HIP events on its stream) and the CPU oracle's throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from dataclasses import replace
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_VALU_TFLOPS = 157.3
+
+# Dominant kernel class per workload (largest summed duration in the rocprofv3 kernel
+# trace of this benchmark; see profiles/).
+DOMINANT = {
+    "llada8b_dual_p1000_g1024": "REF_GATE_UP",
+    "llada8b_prefix_p256_g256": "STEP_GATE_UP",
+    "dream7b_dual_b8_p512_g512": "REF_GATE_UP",
+    "tiny_dual": "STEP_GATE_UP",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def logit_scale(name: str) -> float:
+    p = os.path.join(ROOT, "tests", "golden", "logit_scales.json")
+    if name == "tiny_dual":
+        return synth.WORKLOADS[name].model.logit_scale
+    tab = json.load(open(p))
+    return float(tab[name]["logit_scale"])
+
+
+def kernel_work(cls: str, wl, R_step: int):
+    """Algorithmic (flops, bytes) of one launch of a kernel class."""
+    m = wl.model
+    B, S, d, F, V = wl.batch, wl.seq_len, m.d_model, m.d_ffn, m.vocab
+    D, Hq, Hkv = m.head_dim, m.n_heads, m.n_kv_heads
+    e = 2 if m.dtype == "bf16" else 4
+    Nqkv = (Hq + 2 * Hkv) * D
+    Mr, Ms = B * S, B * R_step
+
+    def lin(M, N, K, out_bytes):
+        return 2.0 * M * N * K, float(N * K * e + M * K * e + M * N * out_bytes)
+    table = {
+        "REF_QKV": lin(Mr, Nqkv, d, e), "REF_O": lin(Mr, d, Hq * D, 8),
+        "REF_GATE_UP": lin(Mr, 2 * F, d, e / 2), "REF_DOWN": lin(Mr, d, F, 8),
+        "STEP_QKV": lin(Ms, Nqkv, d, e), "STEP_O": lin(Ms, d, Hq * D, 8),
+        "STEP_GATE_UP": lin(Ms, 2 * F, d, e / 2), "STEP_DOWN": lin(Ms, d, F, 8),
+        "LM_HEAD": lin(B * wl.block_len, V, d, 4),
+        "REF_ATTN": (4.0 * B * S * S * Hq * D, float(B * (2 * Hq + 2 * Hkv) * S * D * e)),
+        "STEP_ATTN": (4.0 * Ms * S * Hq * D, float(B * 2 * Hkv * S * D * e + 2 * Ms * Hq * D * e)),
+        "CONF_UNMASK": (5.0 * B * wl.block_len * V, float(B * wl.block_len * V * 4)),
+    }
+    return table[cls]
+
+
+def counters_for(cls: str, wl_name: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    tab = json.load(open(p))
+    ent = tab.get(f"{wl_name}:{cls}")
+    if not ent:
+        return None
+    if ent.get("source_sha") != source_sha():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "diffusion_dllm_block_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int):
+    """The oracle (float64, as it stands) on a bounded sample of the workload: one full
+    layer over all S rows (a refresh layer) and one layer over the block rows against the
+    cache plus the LM head and the confidence/unmask rule (a step).  Scaled by the layer
+    count and combined with the GPU run's NFE into generated tokens/s."""
+    from threadpoolctl import threadpool_info
+    from oracle import decode
+    from oracle import model as om
+    m = wl.model
+    wl1 = replace(wl, model=replace(m, n_layers=1))
+    M = om.OracleModel(wl1, dtype=np.float64)
+    for n in ("embed", "final_norm", "lm_head"):
+        M.w(n)
+    for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down"):
+        M.w(n, 0)
+    prompt = synth.make_prompt(wl1)
+    B, P, S, K = wl.batch, wl.prompt_len, wl.seq_len, wl.block_len
+    tokens = np.concatenate([prompt, np.full((B, wl.gen_len), m.mask_id, np.int64)], axis=1)
+    t0 = time.perf_counter()
+    x = om.embed(M, tokens)
+    q, k, v = om.layer_qkv(M, 0, x, np.arange(S))
+    om.layer_rest(M, 0, x, q, k, v)
+    t_ref_layer = time.perf_counter() - t0
+    cache = om.KVCache(1, B, m.n_kv_heads, S, m.head_dim, np.float64)
+    cache.K[0][...] = k
+    cache.V[0][...] = v
+    t0 = time.perf_counter()
+    logits = om.cached_step(M, tokens, cache, P, P + K, wl.cache_mode)
+    t_step_1 = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    conf, arg = decode.confidence_argmax(logits.reshape(B * K, -1), m.mask_id)
+    decode.unmask(tokens[:, P:P + K], conf.reshape(B, K), arg.reshape(B, K), m.mask_id,
+                  wl.threshold)
+    t_dec = time.perf_counter() - t0
+    # a 1-layer cached step = 1 layer + LM head; split the LM head off with a timed call
+    t0 = time.perf_counter()
+    om.lm_head(M, np.zeros((B, K, m.d_model)))
+    t_head = time.perf_counter() - t0
+    t_step_layer = max(t_step_1 - t_head, 0.0)
+    L = m.n_layers
+    t_refresh = L * t_ref_layer
+    t_step = L * t_step_layer + t_head + t_dec
+    total = nfe_refreshes * t_refresh + nfe_steps * t_step
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": round(B * wl.gen_len / total, 4), "unit": "tokens/s", "cores": threads,
+        "kind": "oracle",
+        "sample": (f"oracle float64, 1 of {L} layers timed: full-sequence layer {t_ref_layer:.2f} s, "
+                   f"cached-step layer {t_step_layer:.3f} s, LM head {t_head:.3f} s, decode "
+                   f"{t_dec:.3f} s; scaled x{L} and by the GPU run's NFE ({nfe_steps} steps, "
+                   f"{nfe_refreshes} refreshes); extrapolated"),
+        "sample_seconds": round(t_ref_layer + t_step_1 + t_dec + t_head, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llada8b_dual_p1000_g1024")
+    ap.add_argument("--gen-len", type=int, default=0, help="override (for quick runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--roofline-kernel", default="auto")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the multi-GPU "
+              "layout is a design note, not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from diffusion_dllm_block_amd import binding as bd
+    from diffusion_dllm_block_amd.engine import Model, Session
+
+    lib = bd.load()
+    wl = synth.with_scale(synth.WORKLOADS[a.workload], logit_scale(a.workload))
+    if a.gen_len:
+        wl = replace(wl, gen_len=a.gen_len)
+    log(f"workload {wl.name}: B={wl.batch} P={wl.prompt_len} G={wl.gen_len} K={wl.block_len} "
+        f"mode={wl.cache_mode} scale={wl.model.logit_scale:.4f}")
+    t = time.time()
+    model = Model.synthetic(lib, wl) if wl.model.dtype == "bf16" else \
+        Model.from_host(lib, wl.model, synth.make_weights(wl))
+    sess = Session(model, synth.make_prompt(wl), wl.gen_len, wl.block_len, wl.threshold,
+                   wl.cache_mode)
+    torch.cuda.synchronize()
+    log(f"weights + buffers ready in {time.time() - t:.1f} s")
+
+    for i in range(a.warmup):
+        sess.reset_tokens()
+        _, st = sess.generate()
+        log(f"warmup {i}: {st['ms_total']:.1f} ms, {st['steps']} steps")
+
+    cls = DOMINANT.get(wl.name, "REF_GATE_UP") if a.roofline_kernel == "auto" else a.roofline_kernel
+    cid = bd.KERNEL_CLASSES.index(cls)
+    lib.call("dllm_profile_select", cid)
+    stats = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        sess.reset_tokens()
+        _, st = sess.generate()
+        stats.append(st)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    import ctypes as C
+    n_launch, tot_ms = C.c_int32(), C.c_double()
+    lib.call("dllm_profile_read", C.byref(n_launch), C.byref(tot_ms))
+    lib.call("dllm_profile_select", -1)
+    for i, st in enumerate(stats):
+        log(f"step {i}: {st['ms_total']:.1f} ms ({st['steps']} cached steps, {st['refreshes']} "
+            f"refreshes; refresh {st['ms_refresh']:.1f} ms, steps {st['ms_step']:.1f} ms)")
+
+    toks = wl.batch * wl.gen_len * a.steps
+    value = toks / dt
+    nfe_steps, nfe_ref = stats[-1]["steps"], stats[-1]["refreshes"]
+    R_step = wl.block_len if wl.cache_mode == "dual" else wl.gen_len
+    flops, bytes_ = kernel_work(cls, wl, R_step)
+    avg_s = tot_ms.value / 1e3 / max(1, n_launch.value)
+    mfma = cls.startswith("REF_") and cls != "REF_ATTN" or cls == "REF_ATTN"
+    if mfma:
+        roof = {"bound": "mfma", "achieved": round(flops / avg_s / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(bytes_ / avg_s / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = counters_for(cls, wl.name)
+    roof["kernel"] = cls
+    roof["launches"] = n_launch.value
+    roof["avg_launch_us"] = round(avg_s * 1e6, 2)
+
+    out = {
+        "metric": "generated tokens/sec @1 GPU (LLaDA-8B-shape, DualCache, tau=0.9)",
+        "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(dt / a.steps * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and prompts)",
+        "config": {"workload": wl.name, "batch": wl.batch, "prompt_len": wl.prompt_len,
+                   "gen_len": wl.gen_len, "block_len": wl.block_len, "cache": wl.cache_mode,
+                   "threshold": wl.threshold, "logit_scale": round(wl.model.logit_scale, 4),
+                   "nfe_steps": nfe_steps, "nfe_refreshes": nfe_ref,
+                   "tokens_per_step": round(wl.batch * wl.gen_len / max(1, nfe_steps), 3)},
+        "roofline": roof,
+    }
+    if not a.no_cpu_baseline:
+        del sess, model
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(wl, nfe_steps, nfe_ref)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

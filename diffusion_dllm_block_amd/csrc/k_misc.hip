@@ -1,0 +1,164 @@
+// Small kernels: RoPE table, embedding gather + RMSNorm, RMSNorm, fills, and the
+// device side of the seeded synthetic-input generator.
+#include "common.h"
+#include "kernels.h"
+
+namespace dllm {
+
+// ------------------------------------------------------------------ RoPE table
+// cos/sin [S][D/2] of pos * theta^(-2j/D), evaluated in double, stored fp32.
+__global__ void rope_table_kernel(float* cosb, float* sinb, int S, int D, double theta) {
+  int half = D / 2;
+  int64_t n = (int64_t)S * half;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int pos = (int)(i / half), j = (int)(i % half);
+    double inv = pow(theta, -2.0 * (double)j / (double)D);
+    double a = (double)pos * inv;
+    cosb[i] = (float)cos(a);
+    sinb[i] = (float)sin(a);
+  }
+}
+
+hipError_t launch_rope_table(float* cosb, float* sinb, int S, int D, float theta, hipStream_t st) {
+  int64_t n = (int64_t)S * (D / 2);
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  rope_table_kernel<<<blocks, 256, 0, st>>>(cosb, sinb, S, D, (double)theta);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// One workgroup per row; sum of squares reduced in a fixed order (per-thread
+// sequential, wave butterfly, then the 4 waves in order).
+template <typename T>
+__device__ __forceinline__ void rms_row(const float* xr, const T* g, float eps, int d, T* hr,
+                                        float* red) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) ss += xr[i] * xr[i];
+  ss = wave_sum(ss);
+  int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+  if (l == 0) red[w] = ss;
+  __syncthreads();
+  float tot = 0.f;
+  for (int i = 0; i < (int)(blockDim.x / kWave); ++i) tot += red[i];
+  float r = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += blockDim.x)
+    Elt<T>::store(hr, i, (xr[i] * r) * Elt<T>::load(g, i));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void embed_norm_kernel(const int* tokens, int S, int r0, int R,
+                                                         const T* embed, const T* g, float eps,
+                                                         int d, int V, float* x, T* h) {
+  __shared__ float red[4];
+  int j = blockIdx.x;
+  int b = j / R, i = j % R;
+  int tok = tokens[(int64_t)b * S + r0 + i];
+  tok = min(max(tok, 0), V - 1);  // ids outside [0, V) are not valid input; never read out of bounds
+  const T* er = embed + (int64_t)tok * d;
+  float* xr = x + (int64_t)j * d;
+  for (int c = threadIdx.x; c < d; c += blockDim.x) xr[c] = Elt<T>::load(er, c);
+  __syncthreads();
+  rms_row<T>(xr, g, eps, d, h + (int64_t)j * d, red);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int Rin, int Kout,
+                                                      const T* g, float eps, int d, T* h) {
+  __shared__ float red[4];
+  int j = blockIdx.x;
+  int64_t in_row = (int64_t)(j / Kout) * Rin + (j % Kout);
+  rms_row<T>(x + in_row * d, g, eps, d, h + (int64_t)j * d, red);
+}
+
+hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R, int B,
+                             const void* embed, const void* g, float eps, int d, int V, float* x,
+                             void* h, hipStream_t st) {
+  dim3 grid(B * R);
+  if (dtype == F32)
+    embed_norm_kernel<float><<<grid, 256, 0, st>>>(tokens, S, r0, R, (const float*)embed,
+                                                   (const float*)g, eps, d, V, x, (float*)h);
+  else
+    embed_norm_kernel<uint16_t><<<grid, 256, 0, st>>>(tokens, S, r0, R, (const uint16_t*)embed,
+                                                      (const uint16_t*)g, eps, d, V, x,
+                                                      (uint16_t*)h);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int dtype, const float* x, int rows, int Rin, int Kout, const void* g,
+                          float eps, int d, void* h, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (dtype == F32)
+    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, Rin, Kout, (const float*)g, eps, d, (float*)h);
+  else
+    rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(x, Rin, Kout, (const uint16_t*)g, eps, d,
+                                                   (uint16_t*)h);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fills
+__global__ void fill_i32_kernel(int* p, int64_t n, int v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 2048) blocks = 2048;
+  fill_i32_kernel<<<blocks, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ synthetic inputs
+// SplitMix64 (Steele, Lea and Flood 2014): output i of a stream with state x0 is
+// mix(x0 + (i+1) * GAMMA).  Normal deviates by Irwin-Hall over the four 16-bit fields.
+__device__ __forceinline__ uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+template <typename T>
+__global__ void synth_fill_kernel(T* dst, int64_t n, uint64_t x0, double stdv, int mode) {
+#pragma clang fp contract(off)
+  const double c = 0x1.bb67ae8584caap+0 / 65536.0;  // sqrt(3) / 2^16
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    double v;
+    if (mode == 2) {
+      v = stdv;
+    } else {
+      uint64_t r = sm64_mix(x0 + ((uint64_t)i + 1ull) * 0x9E3779B97F4A7C15ull);
+      int64_t s = (int64_t)(r & 0xFFFF) + (int64_t)((r >> 16) & 0xFFFF) +
+                  (int64_t)((r >> 32) & 0xFFFF) + (int64_t)(r >> 48) - 131070;
+      double z = __dmul_rn((double)s, c);
+      v = __dmul_rn(z, stdv);
+      if (mode == 1) v = __dadd_rn(1.0, v);
+    }
+    Elt<T>::store(dst, i, __double2float_rn(v));
+  }
+}
+
+hipError_t launch_synth_fill(void* dst, int64_t n, int dtype, uint64_t seed, uint32_t tid,
+                             double stdv, int mode, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  uint64_t s = seed ^ ((uint64_t)tid << 32);
+  // first output of a SplitMix64 stream seeded with s (computed on the host)
+  uint64_t z = s + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  uint64_t x0 = z ^ (z >> 31);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (dtype == F32)
+    synth_fill_kernel<float><<<(int)blocks, 256, 0, st>>>((float*)dst, n, x0, stdv, mode);
+  else
+    synth_fill_kernel<uint16_t><<<(int)blocks, 256, 0, st>>>((uint16_t*)dst, n, x0, stdv, mode);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

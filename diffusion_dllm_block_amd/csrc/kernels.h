@@ -1,0 +1,90 @@
+// Launch interface of the libdllm HIP kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dllm {
+
+enum DType { F32 = 0, BF16 = 1 };
+
+// ---------------------------------------------------------------- GEMM epilogues
+// Every GEMM computes acc[m][vc] = sum_k X[m][k] * W[row(vc)][k] over "virtual" output
+// columns vc in tiles of 128, then hands a whole fp32 tile to one of these epilogues.
+enum EpiKind {
+  EPI_STORE = 0,   // y T [M][ldy]      = acc
+  EPI_F32 = 1,     // y fp32 [M][ldy]   = scale * acc
+  EPI_RESID = 2,   // y fp32 [M][ldy]  += acc                (residual add)
+  EPI_SWIGLU = 3,  // virtual tile t = 64 gate rows + 64 up rows; y T [M][F] = silu(g) * u
+  EPI_QKV = 4      // RoPE on q/k, scatter q to [B][Hq][R][D], k/v into the cache
+};
+
+struct EpiArgs {
+  void* y = nullptr;
+  int ldy = 0;
+  float scale = 1.f;
+  int F = 0;                       // SWIGLU: d_ffn
+  // QKV
+  void* qo = nullptr;              // T [B][Hq][R][D]
+  void* kc = nullptr;              // T [B][Hkv][Sp][D]  (this layer's K)
+  void* vtc = nullptr;             // T [B][Hkv][D][Sp]  (this layer's V, transposed)
+  const float* rcos = nullptr;     // [S][D/2]
+  const float* rsin = nullptr;
+  int Hq = 0, Hkv = 0, D = 0, R = 0, pos0 = 0, Sp = 0;
+};
+
+enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2 };
+
+struct GemmPlan {
+  int kind = 0;
+  int mt = 1;            // skinny: 32-row tiles per workgroup (1 or 2)
+  int ntn = 0, ntm = 0;  // tiles along N (virtual) and M
+  int splits = 1, kchunk = 0;
+  size_t part_floats = 0;  // split-K partial buffer
+  int counters = 0;        // split-K arrival counters
+};
+
+GemmPlan gemm_plan(int dtype, int M, int Nv, int K);
+hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
+                       const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
+                       int* counters, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  int kind = 0;          // 0: fp32 simple, 1: bf16 split-KV (R <= 64), 2: bf16 flash
+  int nqt = 0, nchunk = 0;
+  size_t part_floats = 0;
+  int counters = 0;
+};
+AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D);
+hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const void* k,
+                            const void* vt, void* o, int B, int Hq, int Hkv, int R, int S,
+                            int Sp, int D, float* part, int* counters, hipStream_t st);
+
+// ---------------------------------------------------------------- confidence / unmask
+struct ConfPlan {
+  int nsplit = 1, chunk = 0;
+  size_t part_elems = 0;  // per array (m, s, idx)
+  int counters = 0;
+};
+ConfPlan conf_plan(int rows, int V, int B);
+hipError_t launch_conf_unmask(int ldtype, const ConfPlan& p, const void* logits, int B, int K,
+                              int V, int mask_id, float tau, int* tokens, int ld_tokens,
+                              float* conf, int* argmax, int* n_unmasked, int* remaining,
+                              int* unmasked_idx, float* pm, float* ps, int* pi, int* counters,
+                              hipStream_t st);
+
+// ---------------------------------------------------------------- small kernels
+hipError_t launch_rope_table(float* cosb, float* sinb, int S, int D, float theta, hipStream_t st);
+// x[j] = embed[tokens[b*S + r0 + i]] (fp32), h[j] = rmsnorm(x[j]) * g  for j = b*R + i
+hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R, int B,
+                             const void* embed, const void* g, float eps, int d, int V, float* x,
+                             void* h, hipStream_t st);
+// h[j] = rmsnorm(x[in_row(j)]) * g, in_row(j) = (j / Kout) * Rin + j % Kout, j < rows
+hipError_t launch_rmsnorm(int dtype, const float* x, int rows, int Rin, int Kout,
+                          const void* g, float eps, int d, void* h, hipStream_t st);
+hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st);
+hipError_t launch_synth_fill(void* dst, int64_t n, int dtype, uint64_t seed, uint32_t tid,
+                             double stdv, int mode, hipStream_t st);
+
+}  // namespace dllm

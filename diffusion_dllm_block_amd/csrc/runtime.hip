@@ -1,0 +1,616 @@
+// libdllm host runtime: argument validation, workspace planning, the launch sequences of
+// prefill / refresh / block step, the generation loop and the C ABI (include/dllm.h).
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dllm.h"
+#include "../../include/dllm_synth.h"
+#include "kernels.h"
+
+using namespace dllm;
+
+namespace {
+
+thread_local std::string g_err;
+
+dllm_status fail(dllm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIP_TRY(expr)                                                              \
+  do {                                                                             \
+    hipError_t _e = (expr);                                                        \
+    if (_e != hipSuccess)                                                          \
+      return fail(DLLM_E_HIP, "%s failed: %s", #expr, hipGetErrorString(_e));      \
+  } while (0)
+
+// ------------------------------------------------------------------ profiling
+struct Prof {
+  int cls = DLLM_K_NONE;
+  std::vector<hipEvent_t> ev;  // pairs
+  size_t used = 0;             // events recorded
+};
+Prof g_prof;
+
+struct ProfScope {
+  hipStream_t st;
+  bool on;
+  ProfScope(int cls, hipStream_t s) : st(s), on(cls == g_prof.cls) {
+    if (!on) return;
+    if (g_prof.used + 2 > g_prof.ev.size()) {
+      for (int i = 0; i < 256; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+        g_prof.ev.push_back(e);
+      }
+    }
+    (void)hipEventRecord(g_prof.ev[g_prof.used], st);
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(g_prof.ev[g_prof.used + 1], st);
+    g_prof.used += 2;
+  }
+};
+
+// ------------------------------------------------------------------ shapes
+struct Dims {
+  int L, d, Hq, Hkv, D, F, V, mask, dtype, esz;
+  int B, P, G, K, S, Sp, mode, nblocks;
+  float tau, eps, theta, lscale;
+};
+
+constexpr size_t kAlign = 256;
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+dllm_status check_model(const dllm_model_desc* m) {
+  if (!m) return fail(DLLM_E_NULL, "model descriptor is NULL");
+  if (m->dtype != DLLM_F32 && m->dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype %d", m->dtype);
+  if (m->n_layers < 1 || m->d_model < 1 || m->n_heads < 1 || m->n_kv_heads < 1 ||
+      m->head_dim < 2 || m->d_ffn < 1 || m->vocab < 2)
+    return fail(DLLM_E_SHAPE, "model sizes must be positive (vocab >= 2, head_dim >= 2)");
+  if (m->n_heads % m->n_kv_heads) return fail(DLLM_E_SHAPE, "n_heads %% n_kv_heads != 0");
+  if (m->head_dim % 2 || 128 % m->head_dim)
+    return fail(DLLM_E_UNSUPPORTED, "head_dim must be even and divide 128");
+  if (m->d_model % 64 || m->d_ffn % 64 || (m->n_heads * m->head_dim) % 64)
+    return fail(DLLM_E_UNSUPPORTED, "d_model, d_ffn and n_heads*head_dim must be multiples of 64");
+  if (m->dtype == DLLM_BF16 && (m->head_dim != 128 || m->d_model % 128 || m->d_ffn % 128))
+    return fail(DLLM_E_UNSUPPORTED, "bf16 models need head_dim 128 and d_model, d_ffn multiples of 128");
+  if (m->mask_id < 0 || m->mask_id >= m->vocab) return fail(DLLM_E_ARG, "mask_id outside [0, vocab)");
+  if (!std::isfinite(m->rope_theta) || m->rope_theta <= 0.f) return fail(DLLM_E_ARG, "bad rope_theta");
+  if (!std::isfinite(m->norm_eps) || m->norm_eps < 0.f) return fail(DLLM_E_ARG, "bad norm_eps");
+  if (!std::isfinite(m->logit_scale)) return fail(DLLM_E_ARG, "bad logit_scale");
+  if (!m->embed || !m->final_norm || !m->lm_head) return fail(DLLM_E_NULL, "embed/final_norm/lm_head is NULL");
+  if (!m->attn_norm || !m->w_qkv || !m->w_o || !m->ffn_norm || !m->w_gate_up || !m->w_down)
+    return fail(DLLM_E_NULL, "a per-layer weight array is NULL");
+  for (int l = 0; l < m->n_layers; ++l)
+    if (!m->attn_norm[l] || !m->w_qkv[l] || !m->w_o[l] || !m->ffn_norm[l] || !m->w_gate_up[l] ||
+        !m->w_down[l])
+      return fail(DLLM_E_NULL, "layer %d has a NULL weight", l);
+  return DLLM_OK;
+}
+
+dllm_status dims_of(const dllm_model_desc* m, const dllm_seq_desc* s, Dims* o) {
+  dllm_status st = check_model(m);
+  if (st) return st;
+  if (!s) return fail(DLLM_E_NULL, "sequence descriptor is NULL");
+  if (s->batch < 1 || s->prompt_len < 0 || s->gen_len < 1 || s->block_len < 1)
+    return fail(DLLM_E_SHAPE, "batch, gen_len, block_len must be >= 1 and prompt_len >= 0");
+  if (s->gen_len % s->block_len) return fail(DLLM_E_SHAPE, "gen_len %% block_len != 0");
+  if (s->block_len > 64) return fail(DLLM_E_UNSUPPORTED, "block_len > 64");
+  if (s->cache_mode != DLLM_CACHE_PREFIX && s->cache_mode != DLLM_CACHE_DUAL)
+    return fail(DLLM_E_ARG, "bad cache_mode %d", s->cache_mode);
+  if (std::isnan(s->threshold)) return fail(DLLM_E_ARG, "threshold is NaN");
+  Dims& d = *o;
+  d.L = m->n_layers; d.d = m->d_model; d.Hq = m->n_heads; d.Hkv = m->n_kv_heads;
+  d.D = m->head_dim; d.F = m->d_ffn; d.V = m->vocab; d.mask = m->mask_id; d.dtype = m->dtype;
+  d.esz = m->dtype == DLLM_F32 ? 4 : 2;
+  d.B = s->batch; d.P = s->prompt_len; d.G = s->gen_len; d.K = s->block_len;
+  d.S = d.P + d.G; d.Sp = (d.S + 63) / 64 * 64; d.mode = s->cache_mode;
+  d.nblocks = d.G / d.K;
+  d.tau = s->threshold; d.eps = m->norm_eps; d.theta = m->rope_theta; d.lscale = m->logit_scale;
+  if ((double)d.B * d.S > 1e8 || (double)d.S > 1e6) return fail(DLLM_E_UNSUPPORTED, "sequence too long");
+  if (d.dtype == DLLM_F32 && d.S > 12000)
+    return fail(DLLM_E_UNSUPPORTED, "fp32 models support S <= 12000");
+  return DLLM_OK;
+}
+
+// Rows per sequence recomputed by a step of block b.
+int step_rows(const Dims& d, int b) {
+  int s0 = d.P + b * d.K;
+  return d.mode == DLLM_CACHE_DUAL ? d.K : d.S - s0;
+}
+
+struct Ws {
+  size_t x, h, q, o, a, logits, rcos, rsin, gpart, gcnt, apart, acnt, cpm, cps, cpi, ccnt,
+      conf, argmax, nun, rem, total;
+  size_t gpart_floats, apart_floats;
+  int gcnt_n, acnt_n, ccnt_n;
+};
+
+void plan_gemms(const Dims& d, int M, bool lm, size_t* pf, int* cn) {
+  const int Nqkv = (d.Hq + 2 * d.Hkv) * d.D;
+  GemmPlan ps[5] = {gemm_plan(d.dtype, M, Nqkv, d.d), gemm_plan(d.dtype, M, d.d, d.Hq * d.D),
+                    gemm_plan(d.dtype, M, 2 * d.F, d.d), gemm_plan(d.dtype, M, d.d, d.F),
+                    gemm_plan(d.dtype, d.B * d.K, d.V, d.d)};
+  for (int i = 0; i < (lm ? 5 : 4); ++i) {
+    if (ps[i].part_floats > *pf) *pf = ps[i].part_floats;
+    if (ps[i].counters > *cn) *cn = ps[i].counters;
+  }
+}
+
+Ws plan_ws(const Dims& d) {
+  Ws w{};
+  const size_t Mmax = (size_t)d.B * d.S;
+  size_t gpf = 0, apf = 0;
+  int gcn = 0, acn = 0;
+  plan_gemms(d, (int)Mmax, false, &gpf, &gcn);
+  for (int b = 0; b < d.nblocks; ++b) {
+    int R = step_rows(d, b);
+    plan_gemms(d, d.B * R, true, &gpf, &gcn);
+    AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, R, d.S, d.D);
+    if (ap.part_floats > apf) apf = ap.part_floats;
+    if (ap.counters > acn) acn = ap.counters;
+    if (d.mode == DLLM_CACHE_DUAL) break;  // every block has the same row count
+  }
+  ConfPlan cp = conf_plan(d.B * d.K, d.V, d.B);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up(bytes); return o; };
+  w.x = take(Mmax * d.d * 4);
+  w.h = take(Mmax * d.d * d.esz);
+  w.q = take((size_t)d.B * d.Hq * d.S * d.D * d.esz);
+  w.o = take(Mmax * d.Hq * d.D * d.esz);
+  w.a = take(Mmax * d.F * d.esz);
+  w.logits = take((size_t)d.B * d.K * d.V * 4);
+  w.rcos = take((size_t)d.S * (d.D / 2) * 4);
+  w.rsin = take((size_t)d.S * (d.D / 2) * 4);
+  w.gpart = take(gpf * 4);
+  w.apart = take(apf * 4);
+  w.cpm = take(cp.part_elems * 4);
+  w.cps = take(cp.part_elems * 4);
+  w.cpi = take(cp.part_elems * 4);
+  w.conf = take((size_t)d.B * d.K * 4);
+  w.argmax = take((size_t)d.B * d.K * 4);
+  w.nun = take((size_t)d.B * 4);
+  w.rem = take((size_t)d.B * 4);
+  // counters last, contiguous, zeroed at prefill
+  w.gcnt = take((size_t)gcn * 4);
+  w.acnt = take((size_t)acn * 4);
+  w.ccnt = take((size_t)cp.counters * 4);
+  w.total = off;
+  w.gpart_floats = gpf;
+  w.apart_floats = apf;
+  w.gcnt_n = gcn;
+  w.acnt_n = acn;
+  w.ccnt_n = cp.counters;
+  return w;
+}
+
+size_t cache_bytes(const Dims& d) {
+  return (size_t)d.L * 2 * d.B * d.Hkv * d.Sp * d.D * d.esz;
+}
+
+dllm_status check_buffers(const Dims& d, const dllm_seq_desc* s, Ws* w) {
+  if (!s->tokens) return fail(DLLM_E_NULL, "tokens is NULL");
+  if (!s->kv_cache) return fail(DLLM_E_NULL, "kv_cache is NULL");
+  if (!s->workspace) return fail(DLLM_E_NULL, "workspace is NULL");
+  *w = plan_ws(d);
+  if (s->kv_cache_bytes < cache_bytes(d))
+    return fail(DLLM_E_WORKSPACE, "kv_cache_bytes %zu < %zu", s->kv_cache_bytes, cache_bytes(d));
+  if (s->workspace_bytes < w->total)
+    return fail(DLLM_E_WORKSPACE, "workspace_bytes %zu < %zu", s->workspace_bytes, w->total);
+  return DLLM_OK;
+}
+
+// ------------------------------------------------------------------ execution
+struct Ctx {
+  const Dims& d;
+  const dllm_model_desc* m;
+  const dllm_seq_desc* s;
+  Ws w;
+  char* ws;
+  hipStream_t st;
+  template <typename P> P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
+  void* cache_k(int l) const {
+    return (char*)s->kv_cache + (size_t)l * 2 * d.B * d.Hkv * d.Sp * d.D * d.esz;
+  }
+  void* cache_vt(int l) const {
+    return (char*)cache_k(l) + (size_t)d.B * d.Hkv * d.Sp * d.D * d.esz;
+  }
+};
+
+dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const void* W, int M,
+                 int Nv, int K, const EpiArgs& e) {
+  GemmPlan p = gemm_plan(c.d.dtype, M, Nv, K);
+  if (p.part_floats > c.w.gpart_floats || p.counters > c.w.gcnt_n)
+    return fail(DLLM_E_WORKSPACE, "internal: GEMM plan exceeds the workspace plan");
+  ProfScope ps(cls, c.st);
+  HIP_TRY(launch_gemm(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, e, c.at<float>(c.w.gpart),
+                      c.at<int>(c.w.gcnt), c.st));
+  return DLLM_OK;
+}
+
+// Layer stack over R rows per sequence starting at absolute position r0.
+dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
+  const Dims& d = c.d;
+  const int M = d.B * R;
+  float* x = c.at<float>(c.w.x);
+  void* h = c.at<void>(c.w.h);
+  void* q = c.at<void>(c.w.q);
+  void* o = c.at<void>(c.w.o);
+  void* a = c.at<void>(c.w.a);
+  {
+    ProfScope ps(DLLM_K_EMBED_NORM, c.st);
+    HIP_TRY(launch_embed_norm(d.dtype, c.s->tokens, d.S, r0, R, d.B, c.m->embed,
+                              c.m->attn_norm[0], d.eps, d.d, d.V, x, h, c.st));
+  }
+  AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, R, d.S, d.D);
+  if (ap.part_floats > c.w.apart_floats || ap.counters > c.w.acnt_n)
+    return fail(DLLM_E_WORKSPACE, "internal: attention plan exceeds the workspace plan");
+  const int Nqkv = (d.Hq + 2 * d.Hkv) * d.D;
+  for (int l = 0; l < d.L; ++l) {
+    if (l > 0) {
+      ProfScope ps(DLLM_K_RMSNORM, c.st);
+      HIP_TRY(launch_rmsnorm(d.dtype, x, M, R, R, c.m->attn_norm[l], d.eps, d.d, h, c.st));
+    }
+    EpiArgs eq;
+    eq.qo = q; eq.kc = c.cache_k(l); eq.vtc = c.cache_vt(l);
+    eq.rcos = c.at<float>(c.w.rcos); eq.rsin = c.at<float>(c.w.rsin);
+    eq.Hq = d.Hq; eq.Hkv = d.Hkv; eq.D = d.D; eq.R = R; eq.pos0 = r0; eq.Sp = d.Sp;
+    dllm_status st = gemm(c, refresh ? DLLM_K_REF_QKV : DLLM_K_STEP_QKV, EPI_QKV, h, d.d,
+                          c.m->w_qkv[l], M, Nqkv, d.d, eq);
+    if (st) return st;
+    {
+      ProfScope ps(refresh ? DLLM_K_REF_ATTN : DLLM_K_STEP_ATTN, c.st);
+      HIP_TRY(launch_attention(d.dtype, ap, q, c.cache_k(l), c.cache_vt(l), o, d.B, d.Hq, d.Hkv,
+                               R, d.S, d.Sp, d.D, c.at<float>(c.w.apart), c.at<int>(c.w.acnt),
+                               c.st));
+    }
+    if (refresh && l == d.L - 1) break;  // the last layer's tail feeds no K/V
+    EpiArgs er;
+    er.y = x; er.ldy = d.d;
+    st = gemm(c, refresh ? DLLM_K_REF_O : DLLM_K_STEP_O, EPI_RESID, o, d.Hq * d.D, c.m->w_o[l], M,
+              d.d, d.Hq * d.D, er);
+    if (st) return st;
+    {
+      ProfScope ps(DLLM_K_RMSNORM, c.st);
+      HIP_TRY(launch_rmsnorm(d.dtype, x, M, R, R, c.m->ffn_norm[l], d.eps, d.d, h, c.st));
+    }
+    EpiArgs eg;
+    eg.y = a; eg.F = d.F;
+    st = gemm(c, refresh ? DLLM_K_REF_GATE_UP : DLLM_K_STEP_GATE_UP, EPI_SWIGLU, h, d.d,
+              c.m->w_gate_up[l], M, 2 * d.F, d.d, eg);
+    if (st) return st;
+    st = gemm(c, refresh ? DLLM_K_REF_DOWN : DLLM_K_STEP_DOWN, EPI_RESID, a, d.F, c.m->w_down[l], M,
+              d.d, d.F, er);
+    if (st) return st;
+  }
+  return DLLM_OK;
+}
+
+dllm_status do_refresh(const Ctx& c) { return run_layers(c, 0, c.d.S, true); }
+
+dllm_status do_init(const Ctx& c) {
+  const Dims& d = c.d;
+  int ncnt = (int)((c.w.total - c.w.gcnt) / 4);
+  HIP_TRY(launch_fill_i32(c.at<int>(c.w.gcnt), ncnt, 0, c.st));
+  HIP_TRY(launch_rope_table(c.at<float>(c.w.rcos), c.at<float>(c.w.rsin), d.S, d.D, d.theta, c.st));
+  return DLLM_OK;
+}
+
+dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, float* conf,
+                    int* argmax) {
+  const Dims& d = c.d;
+  const int s0 = d.P + b * d.K;
+  const int R = step_rows(d, b);
+  dllm_status st = run_layers(c, s0, R, false);
+  if (st) return st;
+  void* h = c.at<void>(c.w.h);
+  {
+    ProfScope ps(DLLM_K_RMSNORM, c.st);
+    HIP_TRY(launch_rmsnorm(d.dtype, c.at<float>(c.w.x), d.B * d.K, R, d.K, c.m->final_norm,
+                           d.eps, d.d, h, c.st));
+  }
+  float* lg = logits ? logits : c.at<float>(c.w.logits);
+  EpiArgs el;
+  el.y = lg; el.ldy = d.V; el.scale = d.lscale;
+  st = gemm(c, DLLM_K_LM_HEAD, EPI_F32, h, d.d, c.m->lm_head, d.B * d.K, d.V, d.d, el);
+  if (st) return st;
+  ConfPlan cp = conf_plan(d.B * d.K, d.V, d.B);
+  ProfScope ps(DLLM_K_CONF_UNMASK, c.st);
+  HIP_TRY(launch_conf_unmask(F32, cp, lg, d.B, d.K, d.V, d.mask, d.tau, c.s->tokens + s0, d.S,
+                             conf ? conf : c.at<float>(c.w.conf),
+                             argmax ? argmax : c.at<int>(c.w.argmax), n_un, rem, nullptr,
+                             c.at<float>(c.w.cpm), c.at<float>(c.w.cps), c.at<int>(c.w.cpi),
+                             c.at<int>(c.w.ccnt), c.st));
+  return DLLM_OK;
+}
+
+dllm_status setup(const dllm_model_desc* m, const dllm_seq_desc* s, Dims* d, Ws* w) {
+  dllm_status st = dims_of(m, s, d);
+  if (st) return st;
+  return check_buffers(*d, s, w);
+}
+
+double now_ms() {
+  return std::chrono::duration<double, std::milli>(
+             std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+size_t dllm_workspace_bytes(const dllm_model_desc* m, const dllm_seq_desc* s) {
+  Dims d;
+  if (dims_of(m, s, &d)) return 0;
+  return plan_ws(d).total;
+}
+
+size_t dllm_kv_cache_bytes(const dllm_model_desc* m, const dllm_seq_desc* s) {
+  Dims d;
+  if (dims_of(m, s, &d)) return 0;
+  return cache_bytes(d);
+}
+
+dllm_status dllm_prefill_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
+                               dllm_stream_t stream) {
+  Dims d;
+  Ws w;
+  dllm_status st = setup(m, s, &d, &w);
+  if (st) return st;
+  Ctx c{d, m, s, w, (char*)s->workspace, (hipStream_t)stream};
+  st = do_init(c);
+  if (st) return st;
+  return do_refresh(c);
+}
+
+dllm_status dllm_refresh_cache(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
+                               dllm_stream_t stream) {
+  Dims d;
+  Ws w;
+  dllm_status st = setup(m, s, &d, &w);
+  if (st) return st;
+  if (block < 0 || block >= d.nblocks) return fail(DLLM_E_STATE, "block %d outside [0, %d)", block, d.nblocks);
+  Ctx c{d, m, s, w, (char*)s->workspace, (hipStream_t)stream};
+  return do_refresh(c);
+}
+
+dllm_status dllm_block_step(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
+                            dllm_stream_t stream, int32_t* d_n_unmasked, int32_t* d_remaining,
+                            float* d_logits, float* d_conf, int32_t* d_argmax) {
+  Dims d;
+  Ws w;
+  dllm_status st = setup(m, s, &d, &w);
+  if (st) return st;
+  if (block < 0 || block >= d.nblocks) return fail(DLLM_E_STATE, "block %d outside [0, %d)", block, d.nblocks);
+  if (!d_n_unmasked || !d_remaining) return fail(DLLM_E_NULL, "n_unmasked/remaining is NULL");
+  Ctx c{d, m, s, w, (char*)s->workspace, (hipStream_t)stream};
+  return do_step(c, block, d_n_unmasked, d_remaining, d_logits, d_conf, d_argmax);
+}
+
+dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm_stream_t stream,
+                          dllm_stats* out) {
+  Dims d;
+  Ws w;
+  dllm_status st = setup(m, s, &d, &w);
+  if (st) return st;
+  hipStream_t hs = (hipStream_t)stream;
+  Ctx c{d, m, s, w, (char*)s->workspace, hs};
+  int32_t* host = nullptr;  // pinned: [B] remaining + [B*K] block tokens
+  HIP_TRY(hipHostMalloc((void**)&host, sizeof(int32_t) * (d.B + d.B * d.K), hipHostMallocDefault));
+  struct Free { int32_t* p; ~Free() { if (p) (void)hipHostFree(p); } } guard{host};
+  const double t_start = now_ms();
+  double ms_ref = 0, ms_step = 0;
+  int steps = 0, refreshes = 0;
+  for (int b = 0; b < d.nblocks; ++b) {
+    double t0 = now_ms();
+    st = (b == 0) ? do_init(c) : DLLM_OK;
+    if (st) return st;
+    st = do_refresh(c);
+    if (st) return st;
+    ++refreshes;
+    // does the block still hold mask tokens?
+    const int s0 = d.P + b * d.K;
+    HIP_TRY(hipMemcpy2DAsync(host + d.B, d.K * sizeof(int32_t), s->tokens + s0,
+                             (size_t)d.S * sizeof(int32_t), d.K * sizeof(int32_t), d.B,
+                             hipMemcpyDeviceToHost, hs));
+    HIP_TRY(hipStreamSynchronize(hs));
+    ms_ref += now_ms() - t0;
+    bool any = false;
+    for (int i = 0; i < d.B * d.K; ++i) any |= host[d.B + i] == d.mask;
+    int n = 0;
+    t0 = now_ms();
+    while (any) {
+      st = do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+      if (st) return st;
+      HIP_TRY(hipMemcpyAsync(host, c.at<int>(w.rem), d.B * sizeof(int32_t), hipMemcpyDeviceToHost, hs));
+      HIP_TRY(hipStreamSynchronize(hs));
+      ++n;
+      any = false;
+      for (int i = 0; i < d.B; ++i) any |= host[i] != 0;
+      if (n > d.K) return fail(DLLM_E_STATE, "block %d did not finish in %d steps", b, d.K);
+    }
+    ms_step += now_ms() - t0;
+    steps += n;
+    if (out && out->steps_per_block) out->steps_per_block[b] = n;
+  }
+  if (out) {
+    out->steps = steps;
+    out->refreshes = refreshes;
+    out->tokens = d.B * d.G;
+    out->blocks = d.nblocks;
+    out->ms_total = now_ms() - t_start;
+    out->ms_refresh = ms_ref;
+    out->ms_step = ms_step;
+  }
+  return DLLM_OK;
+}
+
+// ---------------------------------------------------------------- kernel-level entries
+static size_t kw_attn(int B, int Hq, int R, int S, int D, int dtype, AttnPlan* p) {
+  *p = attn_plan(dtype, B, Hq, R, S, D);
+  return up((size_t)p->counters * 4) + up(p->part_floats * 4);
+}
+static size_t kw_conf(int rows, int V, int B, ConfPlan* p) {
+  *p = conf_plan(rows, V, B);
+  return up((size_t)p->counters * 4) + 3 * up(p->part_elems * 4);
+}
+
+size_t dllm_kernel_workspace_bytes(int32_t B, int32_t Hq, int32_t R, int32_t S, int32_t D,
+                                   int32_t K, int32_t V) {
+  AttnPlan ap;
+  ConfPlan cp;
+  if (B < 1) return 0;
+  size_t a = (Hq > 0 && R > 0 && S > 0 && D > 0) ? kw_attn(B, Hq, R, S, D, DLLM_BF16, &ap) : 0;
+  size_t c = (K > 0 && V > 0) ? kw_conf(B * K, V, B, &cp) : 0;
+  return a > c ? a : c;
+}
+
+dllm_status dllm_kernel_block_attention(const void* q, const void* k, const void* vt, void* o,
+                                        int32_t B, int32_t Hq, int32_t Hkv, int32_t R, int32_t S,
+                                        int32_t Sp, int32_t D, int32_t dtype, void* ws,
+                                        size_t ws_bytes, dllm_stream_t stream) {
+  if (!q || !k || !vt || !o) return fail(DLLM_E_NULL, "q/k/vt/o is NULL");
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype");
+  if (B < 1 || Hq < 1 || Hkv < 1 || R < 1 || S < 1 || D < 1 || Sp < S)
+    return fail(DLLM_E_SHAPE, "sizes must be positive and Sp >= S");
+  if (Hq % Hkv) return fail(DLLM_E_SHAPE, "Hq %% Hkv != 0");
+  if (dtype == DLLM_BF16 && (D != 128 || Sp % 8))
+    return fail(DLLM_E_UNSUPPORTED, "bf16 attention needs D == 128 and Sp %% 8 == 0");
+  if (dtype == DLLM_F32 && (D > 128 || S > 12000))
+    return fail(DLLM_E_UNSUPPORTED, "fp32 attention needs D <= 128 and S <= 12000");
+  AttnPlan p;
+  size_t need = kw_attn(B, Hq, R, S, D, dtype, &p);
+  if (need && (!ws || ws_bytes < need)) return fail(DLLM_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  int* cnt = (int*)ws;
+  float* part = need ? (float*)((char*)ws + up((size_t)p.counters * 4)) : nullptr;
+  if (p.counters) HIP_TRY(launch_fill_i32(cnt, p.counters, 0, st));
+  ProfScope ps(DLLM_K_STEP_ATTN, st);
+  HIP_TRY(launch_attention(dtype, p, q, k, vt, o, B, Hq, Hkv, R, S, Sp, D, part, cnt, st));
+  return DLLM_OK;
+}
+
+dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dtype, int32_t B,
+                                          int32_t K, int32_t V, int32_t mask_id, float tau,
+                                          int32_t* tokens_block, int32_t ld_tokens, float* conf,
+                                          int32_t* argmax, int32_t* n_unmasked,
+                                          int32_t* remaining, int32_t* unmasked_idx, void* ws,
+                                          size_t ws_bytes, dllm_stream_t stream) {
+  if (!logits || !tokens_block || !conf || !argmax || !n_unmasked || !remaining)
+    return fail(DLLM_E_NULL, "a required pointer is NULL");
+  if (logits_dtype != DLLM_F32 && logits_dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype");
+  if (B < 1 || K < 1 || V < 2 || ld_tokens < K) return fail(DLLM_E_SHAPE, "bad sizes");
+  if (K > 64) return fail(DLLM_E_UNSUPPORTED, "K > 64");
+  if (mask_id < 0 || mask_id >= V) return fail(DLLM_E_ARG, "mask_id outside [0, V)");
+  if (std::isnan(tau)) return fail(DLLM_E_ARG, "tau is NaN");
+  ConfPlan p;
+  size_t need = kw_conf(B * K, V, B, &p);
+  if (!ws || ws_bytes < need) return fail(DLLM_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  int* cnt = (int*)base;
+  size_t off = up((size_t)p.counters * 4);
+  float* pm = (float*)(base + off);
+  float* ps_ = (float*)(base + off + up(p.part_elems * 4));
+  int* pi = (int*)(base + off + 2 * up(p.part_elems * 4));
+  HIP_TRY(launch_fill_i32(cnt, p.counters, 0, st));
+  ProfScope ps(DLLM_K_CONF_UNMASK, st);
+  HIP_TRY(launch_conf_unmask(logits_dtype, p, logits, B, K, V, mask_id, tau, tokens_block,
+                             ld_tokens, conf, argmax, n_unmasked, remaining, unmasked_idx, pm, ps_,
+                             pi, cnt, st));
+  return DLLM_OK;
+}
+
+size_t dllm_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype) {
+  if (M < 1 || N < 1 || K < 1) return 0;
+  GemmPlan p = gemm_plan(dtype, M, N, K);
+  return up((size_t)p.counters * 4) + up(p.part_floats * 4) + kAlign;
+}
+
+dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
+                               int32_t K, int32_t dtype, int32_t mode, float scale, void* ws,
+                               size_t ws_bytes, dllm_stream_t stream) {
+  if (!x || !w || !y) return fail(DLLM_E_NULL, "x/w/y is NULL");
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype");
+  if (mode < 0 || mode > 2) return fail(DLLM_E_ARG, "bad mode");
+  if (M < 1 || N < 1 || K < 1) return fail(DLLM_E_SHAPE, "sizes must be positive");
+  if (dtype == DLLM_BF16 && K % 128) return fail(DLLM_E_UNSUPPORTED, "bf16 needs K %% 128 == 0");
+  if (dtype == DLLM_F32 && K % 16) return fail(DLLM_E_UNSUPPORTED, "fp32 needs K %% 16 == 0");
+  GemmPlan p = gemm_plan(dtype, M, N, K);
+  size_t need = up((size_t)p.counters * 4) + up(p.part_floats * 4);
+  if (need && (!ws || ws_bytes < need)) return fail(DLLM_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
+  hipStream_t st = (hipStream_t)stream;
+  int* cnt = (int*)ws;
+  float* part = need ? (float*)((char*)ws + up((size_t)p.counters * 4)) : nullptr;
+  if (p.counters) HIP_TRY(launch_fill_i32(cnt, p.counters, 0, st));
+  EpiArgs e;
+  e.y = y; e.ldy = N; e.scale = scale;
+  int epi = mode == 0 ? EPI_STORE : mode == 1 ? EPI_F32 : EPI_RESID;
+  HIP_TRY(launch_gemm(dtype, epi, p, x, K, w, M, N, K, e, part, cnt, st));
+  return DLLM_OK;
+}
+
+dllm_status dllm_synth_fill(void* dst, int64_t n, int32_t dtype, uint64_t seed,
+                            uint32_t tensor_id, double stdv, int32_t mode, dllm_stream_t stream) {
+  if (!dst && n > 0) return fail(DLLM_E_NULL, "dst is NULL");
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype");
+  if (mode < 0 || mode > 2) return fail(DLLM_E_ARG, "bad mode");
+  if (n < 0) return fail(DLLM_E_SHAPE, "n < 0");
+  HIP_TRY(launch_synth_fill(dst, n, dtype, seed, tensor_id, stdv, mode, (hipStream_t)stream));
+  return DLLM_OK;
+}
+
+const char* dllm_status_string(dllm_status st) {
+  switch (st) {
+    case DLLM_OK: return "ok";
+    case DLLM_E_NULL: return "null pointer";
+    case DLLM_E_SHAPE: return "inconsistent shape";
+    case DLLM_E_UNSUPPORTED: return "unsupported configuration";
+    case DLLM_E_WORKSPACE: return "buffer too small";
+    case DLLM_E_HIP: return "HIP runtime error";
+    case DLLM_E_STATE: return "bad block index or state";
+    case DLLM_E_ARG: return "bad argument";
+  }
+  return "unknown status";
+}
+
+const char* dllm_last_error(void) { return g_err.c_str(); }
+
+dllm_status dllm_profile_select(int32_t kernel_class) {
+  if (kernel_class < DLLM_K_NONE || kernel_class >= DLLM_K_COUNT)
+    return fail(DLLM_E_ARG, "bad kernel class %d", kernel_class);
+  g_prof.cls = kernel_class;
+  g_prof.used = 0;
+  return DLLM_OK;
+}
+
+dllm_status dllm_profile_read(int32_t* launches, double* total_ms) {
+  double tot = 0;
+  for (size_t i = 0; i + 1 < g_prof.used; i += 2) {
+    HIP_TRY(hipEventSynchronize(g_prof.ev[i + 1]));
+    float ms = 0;
+    HIP_TRY(hipEventElapsedTime(&ms, g_prof.ev[i], g_prof.ev[i + 1]));
+    tot += ms;
+  }
+  if (launches) *launches = (int32_t)(g_prof.used / 2);
+  if (total_ms) *total_ms = tot;
+  g_prof.used = 0;
+  return DLLM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+"""Python-side ownership of device buffers for libdllm: a Model (weights) and a Session
+(tokens, KV cache, workspace of one batch being generated).
+
+torch provides the device allocations and the stream; every computation is a library
+call (binding.py).
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from . import binding as bd
+
+_WEIGHT_NAMES = ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _tdtype(dtype: int):
+    torch = _torch()
+    return torch.float32 if dtype == bd.F32 else torch.bfloat16
+
+
+class Model:
+    """Weights on the device.  ``shape`` needs the attributes n_layers, d_model, n_heads,
+    n_kv_heads, head_dim, d_ffn, vocab, mask_id, rope_theta, norm_eps, logit_scale and
+    dtype ("f32" or "bf16")."""
+
+    def __init__(self, lib: bd.Lib, shape, tensors: dict):
+        self.lib, self.shape, self.t = lib, shape, tensors
+        self.dtype = bd.F32 if shape.dtype == "f32" else bd.BF16
+        L = shape.n_layers
+        self._arrays = {}
+        for n in _WEIGHT_NAMES:
+            arr = (C.c_void_p * L)(*[tensors[f"{n}.{l}"].data_ptr() for l in range(L)])
+            self._arrays[n] = arr
+        self.desc = bd.ModelDesc(
+            n_layers=L, d_model=shape.d_model, n_heads=shape.n_heads, n_kv_heads=shape.n_kv_heads,
+            head_dim=shape.head_dim, d_ffn=shape.d_ffn, vocab=shape.vocab, mask_id=shape.mask_id,
+            rope_theta=shape.rope_theta, norm_eps=shape.norm_eps, logit_scale=shape.logit_scale,
+            dtype=self.dtype, embed=tensors["embed"].data_ptr(),
+            final_norm=tensors["final_norm"].data_ptr(), lm_head=tensors["lm_head"].data_ptr(),
+            **{n: C.cast(self._arrays[n], C.POINTER(C.c_void_p)) for n in _WEIGHT_NAMES})
+
+    def with_logit_scale(self, scale: float) -> "Model":
+        from dataclasses import replace
+        return Model(self.lib, replace(self.shape, logit_scale=float(scale)), self.t)
+
+    @staticmethod
+    def from_host(lib: bd.Lib, shape, weights: dict, device="cuda") -> "Model":
+        """Upload host arrays: float32 values (f32 models) or uint16 bf16 bit patterns."""
+        torch = _torch()
+        t = {}
+        for k, a in weights.items():
+            if shape.dtype == "f32":
+                t[k] = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+            else:
+                b = np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)
+                t[k] = torch.from_numpy(b).view(torch.bfloat16).to(device)
+        return Model(lib, shape, t)
+
+    @staticmethod
+    def synthetic(lib: bd.Lib, wl, device="cuda", stream=None) -> "Model":
+        """Seeded random-init weights made on the device by the library's generator
+        (bit-identical to the host generator in ``synth``)."""
+        import synth
+        torch = _torch()
+        m = wl.model
+        dt = bd.F32 if m.dtype == "f32" else bd.BF16
+        st = bd.stream_handle(stream)
+        t = {}
+        for name, layer, tid, shape, std, is_norm in synth.weight_specs(m, wl.norm_gain_std):
+            x = torch.empty(shape, dtype=_tdtype(dt), device=device)
+            if is_norm:
+                mode, s = (2, 1.0) if std == 0.0 else (1, std)
+            else:
+                mode, s = 0, std
+            lib.call("dllm_synth_fill", bd.ptr(x), x.numel(), dt, wl.model_seed, tid, s, mode, st)
+            t[name if layer < 0 else f"{name}.{layer}"] = x
+        return Model(lib, m, t)
+
+
+class Session:
+    """Tokens, KV cache and workspace of one batch of sequences."""
+
+    def __init__(self, model: Model, prompt, gen_len: int, block_len: int, threshold: float,
+                 mode: str, device="cuda"):
+        torch = _torch()
+        self.model, self.lib = model, model.lib
+        prompt = torch.as_tensor(np.asarray(prompt), dtype=torch.int32)
+        B, P = prompt.shape
+        self.B, self.P, self.G, self.K = B, P, gen_len, block_len
+        self.S = P + gen_len
+        self.n_blocks = gen_len // block_len if block_len > 0 else 0
+        toks = torch.full((B, self.S), model.shape.mask_id, dtype=torch.int32)
+        toks[:, :P] = prompt
+        self.tokens = toks.to(device)
+        self.mode = bd.CACHE_DUAL if mode == "dual" else bd.CACHE_PREFIX
+        self.desc = bd.SeqDesc(batch=B, prompt_len=P, gen_len=gen_len, block_len=block_len,
+                               cache_mode=self.mode, threshold=threshold,
+                               tokens=self.tokens.data_ptr())
+        mp, sp = C.byref(model.desc), C.byref(self.desc)
+        cb = self.lib.raw("dllm_kv_cache_bytes")(mp, sp)
+        wb = self.lib.raw("dllm_workspace_bytes")(mp, sp)
+        if cb == 0 or wb == 0:
+            # report why through a call that validates
+            self.lib.check(self.lib.raw("dllm_prefill_cache")(mp, sp, None), "Session")
+        self.cache = torch.empty(cb, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(wb, dtype=torch.uint8, device=device)
+        self.desc.kv_cache = self.cache.data_ptr()
+        self.desc.kv_cache_bytes = cb
+        self.desc.workspace = self.ws.data_ptr()
+        self.desc.workspace_bytes = wb
+        self.n_unmasked = torch.zeros(B, dtype=torch.int32, device=device)
+        self.remaining = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def _args(self):
+        return C.byref(self.model.desc), C.byref(self.desc)
+
+    def prefill(self, stream=None):
+        self.lib.call("dllm_prefill_cache", *self._args(), bd.stream_handle(stream))
+
+    def refresh(self, block: int, stream=None):
+        self.lib.call("dllm_refresh_cache", *self._args(), block, bd.stream_handle(stream))
+
+    def step(self, block: int, logits: bool = True, stream=None) -> dict:
+        torch = _torch()
+        dev = self.tokens.device
+        out = {"n_unmasked": self.n_unmasked, "remaining": self.remaining}
+        lg = torch.empty((self.B * self.K, self.model.shape.vocab), dtype=torch.float32,
+                         device=dev) if logits else None
+        conf = torch.empty((self.B, self.K), dtype=torch.float32, device=dev)
+        arg = torch.empty((self.B, self.K), dtype=torch.int32, device=dev)
+        self.lib.call("dllm_block_step", *self._args(), block, bd.stream_handle(stream),
+                      bd.ptr(self.n_unmasked), bd.ptr(self.remaining), bd.ptr(lg), bd.ptr(conf),
+                      bd.ptr(arg))
+        out.update(logits=lg, conf=conf, argmax=arg)
+        return out
+
+    def generate(self, stream=None):
+        spb = (C.c_int32 * max(1, self.n_blocks))()
+        st = bd.Stats(steps_per_block=spb)
+        self.lib.call("dllm_generate", *self._args(), bd.stream_handle(stream), C.byref(st))
+        stats = {"steps": st.steps, "refreshes": st.refreshes, "tokens": st.tokens,
+                 "blocks": st.blocks, "ms_total": st.ms_total, "ms_refresh": st.ms_refresh,
+                 "ms_step": st.ms_step, "steps_per_block": list(spb)[: self.n_blocks]}
+        return self.tokens[:, self.P:].cpu().numpy(), stats
+
+    def reset_tokens(self, prompt=None):
+        """Put the generated span back to mask tokens (and optionally a new prompt)."""
+        torch = _torch()
+        self.tokens[:, self.P:] = self.model.shape.mask_id
+        if prompt is not None:
+            self.tokens[:, :self.P] = torch.as_tensor(np.asarray(prompt), dtype=torch.int32,
+                                                      device=self.tokens.device)

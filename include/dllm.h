@@ -1,0 +1,233 @@
+/*
+ * libdllm — one denoising step of block-wise masked-diffusion LLM generation with an
+ * approximate KV cache and confidence-aware parallel decoding (Fast-dLLM), for AMD
+ * MI355X (gfx950).
+ *
+ * The method, as described by
+ *   [A] the ccyt168.com Fast-dLLM article, section 1.1 "Block-Wise KV Cache" and
+ *       section 1.2 "Confidence-Aware Parallel Decoding", and
+ *   [B] the techwalker.com explainer "Fast-dLLM: NVIDIA researchers accelerate
+ *       diffusion LLMs without training via KV cache and parallel decoding", sections
+ *       "Core innovation: a KV cache suited to diffusion models" and "Solving the
+ *       quality loss of parallel decoding":
+ *   - the generated span is cut into blocks decoded left to right;
+ *   - before a block, the KV of every position is computed by a full bidirectional
+ *     forward and kept; after the block it is recomputed ([B], steps 1 and 2);
+ *   - DualCache keeps the prompt prefix and the masked suffix; prefix mode keeps only
+ *     the prefix ([A] 1.1, [B]);
+ *   - each step decodes, in parallel, every masked position of the block whose
+ *     confidence (the probability the model gives its argmax token) reaches the
+ *     threshold; the others wait ([A] 1.2, [B]).
+ * Readings where the pages are silent (each used identically by the CPU oracle):
+ *   the mask token is never emitted; confidence >= threshold; argmax ties go to the
+ *   lowest token id; a sequence with masked block positions but none at the threshold
+ *   decodes its single most confident one (lowest position on ties); a refresh decodes
+ *   nothing; sequences of a batch move through blocks in lockstep.
+ *
+ * Model (readings; the pages only name LLaDA and Dream): pre-norm transformer with
+ * RMSNorm, rotate-half RoPE, SwiGLU FFN, no biases, untied LM head, grouped-query
+ * attention allowed (query head h reads KV head h / (n_heads / n_kv_heads)),
+ * bidirectional attention (no mask), LM-head output multiplied by logit_scale.
+ *
+ * Precision.  DLLM_F32: every tensor fp32.  DLLM_BF16: weights and KV cache bf16;
+ * residual stream, logits and confidences fp32; RMSNorm outputs, post-RoPE q/k, v,
+ * attention outputs and SwiGLU outputs rounded to bf16 (nearest even); all
+ * accumulation fp32.
+ *
+ * Memory and ownership.  Every pointer in a descriptor is device memory owned by the
+ * caller (the per-layer pointer arrays themselves are host arrays).  The library
+ * allocates no device memory and keeps no pointer after a call returns.
+ *
+ * Errors.  Every call returns a dllm_status and never throws.  Arguments are checked
+ * on the host before anything is enqueued, so an error leaves tokens, cache and
+ * workspace untouched; dllm_last_error() gives a one-line reason (thread-local).
+ * DLLM_E_HIP means a HIP call failed after work was enqueued: tokens and cache are
+ * then unspecified; restore the tokens of the last block boundary and call
+ * dllm_prefill_cache / dllm_refresh_cache again.
+ *
+ * Streams.  prefill, refresh, block_step and the kernel-level calls only enqueue on
+ * `stream`; their outputs are valid once the stream reaches that point.  dllm_generate
+ * is synchronous.  One sequence descriptor (tokens + cache + workspace) must not be
+ * driven from two streams at once.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* dllm_stream_t; /* a hipStream_t; NULL is the null stream */
+
+typedef enum {
+  DLLM_OK = 0,
+  DLLM_E_NULL = -1,        /* a required pointer is NULL                               */
+  DLLM_E_SHAPE = -2,       /* inconsistent sizes (e.g. gen_len % block_len != 0)        */
+  DLLM_E_UNSUPPORTED = -3, /* valid but not implemented (e.g. block_len > 64)           */
+  DLLM_E_WORKSPACE = -4,   /* workspace or cache buffer smaller than required           */
+  DLLM_E_HIP = -5,         /* a HIP runtime call failed                                 */
+  DLLM_E_STATE = -6,       /* block index out of range                                  */
+  DLLM_E_ARG = -7          /* bad scalar argument (NaN threshold, bad enum, mask id)    */
+} dllm_status;
+
+typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
+typedef enum { DLLM_CACHE_PREFIX = 1, DLLM_CACHE_DUAL = 2 } dllm_cache_mode;
+
+/* Model weights.  Shapes are row-major; "T" is float (DLLM_F32) or bf16 (DLLM_BF16).
+ * Supported: head_dim divides 128 (and is even); n_heads % n_kv_heads == 0;
+ * d_model, d_ffn and n_heads*head_dim multiples of 64; for DLLM_BF16 also head_dim ==
+ * 128 and d_model, d_ffn multiples of 128.  mask_id in [0, vocab).                   */
+typedef struct {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, mask_id;
+  float rope_theta, norm_eps, logit_scale;
+  int32_t dtype;                      /* dllm_dtype                                      */
+  const void* embed;                  /* T [vocab, d_model]                              */
+  const void* final_norm;             /* T [d_model]                                     */
+  const void* lm_head;                /* T [vocab, d_model]                              */
+  const void* const* attn_norm;       /* n_layers x T [d_model]                          */
+  const void* const* w_qkv;           /* n_layers x T [(n_heads+2*n_kv_heads)*head_dim, d_model]:
+                                         q rows, then k rows, then v rows               */
+  const void* const* w_o;             /* n_layers x T [d_model, n_heads*head_dim]        */
+  const void* const* ffn_norm;        /* n_layers x T [d_model]                          */
+  const void* const* w_gate_up;       /* n_layers x T [2*d_ffn, d_model]: gate rows first */
+  const void* const* w_down;          /* n_layers x T [d_model, d_ffn]                   */
+} dllm_model_desc;
+
+/* One batch of sequences being generated.  S = prompt_len + gen_len.
+ * tokens: device int32 [batch, S], in/out; the generated span must hold mask_id before
+ *   the first call; decoded tokens are written in place.
+ * kv_cache: device buffer of dllm_kv_cache_bytes(); layout per layer l (in elements of
+ *   T, Sp = S rounded up to a multiple of 64):
+ *     K  at l*2*B*Hkv*Sp*D                 : [B][Hkv][Sp][D]  (post-RoPE keys)
+ *     Vt at l*2*B*Hkv*Sp*D + B*Hkv*Sp*D    : [B][Hkv][D][Sp]  (values, transposed)
+ *   positions >= S are never read.
+ * workspace: device scratch of dllm_workspace_bytes(); dllm_prefill_cache initialises
+ *   it and must run before the first dllm_block_step / dllm_refresh_cache.           */
+typedef struct {
+  int32_t batch, prompt_len, gen_len, block_len;
+  int32_t cache_mode;                 /* dllm_cache_mode                                 */
+  float threshold;                    /* confidence threshold, e.g. 0.9                  */
+  int32_t* tokens;
+  void* kv_cache;
+  size_t kv_cache_bytes;
+  void* workspace;
+  size_t workspace_bytes;
+} dllm_seq_desc;
+
+typedef struct {
+  int32_t steps;                      /* cached denoising steps run                      */
+  int32_t refreshes;                  /* full forwards run (prefill included)            */
+  int32_t tokens;                     /* tokens generated (batch * gen_len)              */
+  int32_t blocks;
+  double ms_total, ms_refresh, ms_step; /* host wall clock, stream-synchronised          */
+  int32_t* steps_per_block;           /* optional host array [gen_len/block_len], or NULL */
+} dllm_stats;
+
+/* Sizes (host only, no device work).  Return 0 if the descriptors are invalid.       */
+size_t dllm_workspace_bytes(const dllm_model_desc* m, const dllm_seq_desc* s);
+size_t dllm_kv_cache_bytes(const dllm_model_desc* m, const dllm_seq_desc* s);
+
+/* Prefill = the full forward before block 0 ([B] step 1): initialises the workspace
+ * and writes every layer's K/V for all S positions.  Decodes nothing.               */
+dllm_status dllm_prefill_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
+                               dllm_stream_t stream);
+
+/* Refresh after block `block` is finished ([B] step 2): full bidirectional forward
+ * over all S positions of the current tokens; K/V rewritten in place.  The last
+ * layer's output projection and FFN are skipped (they do not feed any K/V).
+ * block in [0, gen_len/block_len).  Decodes nothing.                                */
+dllm_status dllm_refresh_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
+                               int32_t block, dllm_stream_t stream);
+
+/* One cached denoising step of block `block` ([A] 1.1 and 1.2):
+ *   DualCache: the block rows [s0, s1) are recomputed through every layer and attend
+ *   to all S cached keys (their own K/V written in place first); prefix mode: rows
+ *   [s0, S) are recomputed and only [0, s0) comes from the cache.  Then the final
+ *   norm and LM head over the block rows, the vocab-wide confidence/argmax (mask id
+ *   excluded), and the threshold unmask, which writes decoded tokens into `tokens`.
+ * Outputs (device, may be NULL unless stated):
+ *   d_n_unmasked [batch] int32 (required): tokens decoded this step per sequence;
+ *   d_remaining  [batch] int32 (required): mask tokens left in the block;
+ *   d_logits [batch*block_len, vocab] fp32: the block rows' logits;
+ *   d_conf [batch, block_len] fp32 and d_argmax [batch, block_len] int32.           */
+dllm_status dllm_block_step(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
+                            dllm_stream_t stream, int32_t* d_n_unmasked, int32_t* d_remaining,
+                            float* d_logits, float* d_conf, int32_t* d_argmax);
+
+/* Whole generation: prefill, then for every block cached steps until the block has no
+ * mask token left (one 4*batch-byte device-to-host read per step), then a refresh
+ * (not after the last block).  Synchronous.  `out` may be NULL.                     */
+dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s,
+                          dllm_stream_t stream, dllm_stats* out);
+
+/* ---- kernel-level entries (single stages on caller buffers) ---------------------- */
+
+/* Workspace needed by the two kernel-level calls below: the attention part for
+ * (B, Hq, R, S, D) when all are positive, the confidence part for B sequences of K
+ * block positions over a vocabulary of V when K and V are positive; the larger of the
+ * two.  Returns 0 if B < 1.                                                          */
+size_t dllm_kernel_workspace_bytes(int32_t B, int32_t Hq, int32_t R, int32_t S, int32_t D,
+                                   int32_t K, int32_t V);
+
+/* Non-causal attention of R query rows per (sequence, query head) against S cached
+ * keys ([A] 1.1: the block's queries read the cached KV of all positions).
+ *   q  T [B][Hq][R][D];  k T [B][Hkv][Sp][D];  vt T [B][Hkv][D][Sp]  (Sp >= S; keys
+ *   >= S ignored);  o T [B][R][Hq*D]  (row-major, ready for the output projection).
+ *   o = softmax(q k^T / sqrt(D)) v over all S keys, fp32 softmax and accumulation.
+ * Supported: DLLM_BF16 with D == 128, or DLLM_F32 with D <= 128; Hq % Hkv == 0.     */
+dllm_status dllm_kernel_block_attention(const void* q, const void* k, const void* vt, void* o,
+                                        int32_t B, int32_t Hq, int32_t Hkv, int32_t R,
+                                        int32_t S, int32_t Sp, int32_t D, int32_t dtype,
+                                        void* ws, size_t ws_bytes, dllm_stream_t stream);
+
+/* Vocab-wide confidence and threshold unmask for B sequences of K block positions
+ * ([A] 1.2).  logits T_l [B*K][V] with T_l = fp32 or bf16 (logits_dtype).  Per row:
+ * m = max over v != mask_id, conf = 1 / sum_{v != mask_id} exp(z_v - m), argmax the
+ * lowest id reaching m.  Then per sequence: U = {masked i : conf_i >= tau}, or the
+ * most confident masked position if U is empty and something is masked;
+ * tokens_block[b][i] = argmax for i in U.
+ *   tokens_block int32 [B][K] (in/out, row stride ld_tokens);
+ *   conf fp32 [B*K], argmax int32 [B*K], n_unmasked int32 [B], remaining int32 [B]
+ *   (all required); unmasked_idx int32 [B][K] optional: the positions decoded this
+ *   step in increasing order, then -1.  K <= 64.                                     */
+dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dtype, int32_t B,
+                                          int32_t K, int32_t V, int32_t mask_id, float tau,
+                                          int32_t* tokens_block, int32_t ld_tokens,
+                                          float* conf, int32_t* argmax, int32_t* n_unmasked,
+                                          int32_t* remaining, int32_t* unmasked_idx, void* ws,
+                                          size_t ws_bytes, dllm_stream_t stream);
+
+/* y = x W^T for x T [M][K], W T [N][K].  mode 0: y T [M][N]; mode 1: y fp32 [M][N] =
+ * scale * x W^T; mode 2: y fp32 [M][N] += x W^T (residual add).  Same kernels as the
+ * model path (MFMA for DLLM_BF16: K % 128 == 0).  ws from dllm_linear_workspace_bytes. */
+size_t dllm_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype);
+dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
+                               int32_t K, int32_t dtype, int32_t mode, float scale, void* ws,
+                               size_t ws_bytes, dllm_stream_t stream);
+
+/* ---- diagnostics -------------------------------------------------------------------- */
+
+const char* dllm_status_string(dllm_status st);
+const char* dllm_last_error(void);
+
+/* Per-kernel-class timing with HIP events on the launching stream.  Select one class
+ * (or -1 for none); every later launch of that class is bracketed by two events;
+ * dllm_profile_read() synchronises on the recorded events and returns the number of
+ * launches and their summed duration, then clears the record.                       */
+typedef enum {
+  DLLM_K_NONE = -1,
+  DLLM_K_EMBED_NORM = 0, DLLM_K_RMSNORM, DLLM_K_STEP_QKV, DLLM_K_STEP_ATTN, DLLM_K_STEP_O,
+  DLLM_K_STEP_GATE_UP, DLLM_K_STEP_DOWN, DLLM_K_LM_HEAD, DLLM_K_CONF_UNMASK,
+  DLLM_K_REF_QKV, DLLM_K_REF_ATTN, DLLM_K_REF_O, DLLM_K_REF_GATE_UP, DLLM_K_REF_DOWN,
+  DLLM_K_COUNT
+} dllm_kernel_class;
+dllm_status dllm_profile_select(int32_t kernel_class);
+dllm_status dllm_profile_read(int32_t* launches, double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */

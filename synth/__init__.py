@@ -30,6 +30,7 @@ range reduction), uniform on [0, n).
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -105,18 +106,32 @@ def normal_fp32(seed: int, tensor_id: int, idx: np.ndarray, std: float = 1.0) ->
 
 
 def normal_tensor(seed: int, tensor_id: int, shape, std: float = 1.0,
-                  dtype: str = "f32", chunk: int = 1 << 24) -> np.ndarray:
+                  dtype: str = "f32", chunk: int = 1 << 22, threads: int | None = None) -> np.ndarray:
     """Whole tensor in row-major element order.
 
     dtype "f32" returns float32 values; "bf16" returns the uint16 bit patterns of
-    the bf16 values (use :func:`bf16_bits_to_fp32` to read them).
+    the bf16 values (use :func:`bf16_bits_to_fp32` to read them).  Large tensors are
+    produced by several threads (numpy releases the GIL); the values do not depend on
+    the thread count.
     """
     n = int(np.prod(shape)) if len(shape) else 1
     out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
-    for a in range(0, n, chunk):
+
+    def part(a):
         b = min(n, a + chunk)
         v = normal_fp32(seed, tensor_id, np.arange(a, b, dtype=np.uint64), std)
         out[a:b] = v if dtype == "f32" else fp32_to_bf16_bits(v)
+
+    starts = range(0, n, chunk)
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    if n <= chunk or threads <= 1:
+        for a in starts:
+            part(a)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(part, starts))
     return out.reshape(shape)
 
 

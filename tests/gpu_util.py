@@ -1,0 +1,85 @@
+"""Helpers shared by the GPU tests: host <-> device conversion and the comparison
+protocol for decisions taken from floating-point confidences."""
+import numpy as np
+
+import synth
+
+
+def dev_bf16(bits: np.ndarray, device="cuda"):
+    import torch
+    b = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(b).view(torch.bfloat16).to(device)
+
+
+def dev_f32(a: np.ndarray, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def host(t) -> np.ndarray:
+    """Device tensor -> float64 numpy (bf16 decoded exactly)."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return synth.bf16_bits_to_fp32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.cpu().numpy().astype(np.float64)
+
+
+def rel_inf(got, ref) -> float:
+    """max |got - ref| / max |ref| (per whole array)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+MARGIN = 1e-3
+
+
+def decision_margin_ok(conf, tau, masked, margin=MARGIN):
+    """Per sequence: True where the threshold decisions are not within ``margin`` of a
+    flip: every masked confidence is > margin away from tau, and if the forced-pick
+    path is taken, the top masked confidence leads the runner-up by > margin."""
+    conf = np.asarray(conf, np.float64)
+    ok = np.ones(conf.shape[0], bool)
+    for b in range(conf.shape[0]):
+        c = conf[b][masked[b]]
+        if c.size == 0:
+            continue
+        if np.any(np.abs(c - tau) <= margin):
+            ok[b] = False
+            continue
+        if not np.any(c >= tau) and c.size > 1:
+            s = np.sort(c)[::-1]
+            if s[0] - s[1] <= margin:
+                ok[b] = False
+    return ok
+
+
+def top2_gap(logits_row: np.ndarray, mask_id: int) -> float:
+    """Probability gap between the top two tokens of a row (mask excluded)."""
+    z = np.array(logits_row, np.float64)
+    z[mask_id] = -np.inf
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    s = np.sort(p)[::-1]
+    return float(s[0] - s[1])
+
+
+def safe_sequences(conf_ref, conf_unc, tau, masked):
+    """Per sequence: True where no threshold decision or forced pick can flip given an
+    absolute confidence uncertainty ``conf_unc`` per position ([B, K] or scalar)."""
+    conf = np.asarray(conf_ref, np.float64)
+    unc = np.broadcast_to(np.asarray(conf_unc, np.float64), conf.shape)
+    ok = np.ones(conf.shape[0], bool)
+    for b in range(conf.shape[0]):
+        m = masked[b]
+        c, u = conf[b][m], unc[b][m]
+        if c.size == 0:
+            continue
+        if np.any(np.abs(c - tau) <= u):
+            ok[b] = False
+            continue
+        if not np.any(c >= tau) and c.size > 1:
+            order = np.argsort(-c, kind="stable")
+            if c[order[0]] - c[order[1]] <= u[order[0]] + u[order[1]]:
+                ok[b] = False
+    return ok

@@ -1,0 +1,176 @@
+"""GPU parity of the whole decode path (prefill, refresh, cached steps, generate) against
+the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+from dataclasses import replace
+
+import synth
+from gpu_util import decision_margin_ok, host, rel_inf, safe_sequences
+from oracle import decode
+from oracle import model as om
+from oracle.generate import Session as OSession
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from diffusion_dllm_block_amd import binding as bd  # noqa: E402
+from diffusion_dllm_block_amd.engine import Model, Session  # noqa: E402
+
+
+def gpu_model(lib, wl):
+    return Model.from_host(lib, wl.model, synth.make_weights(wl))
+
+
+def teacher_forced(lib, wl, logits_tol, fp32_decisions):
+    """Step both sides from the oracle's token state; compare every step."""
+    m = wl.model
+    M = om.OracleModel(wl)
+    prompt = synth.make_prompt(wl)
+    osess = OSession(M, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+    gsess = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, wl.threshold,
+                    wl.cache_mode)
+    worst = 0.0
+    checked = excluded = 0
+    for b in range(osess.n_blocks):
+        osess.refresh()
+        if b == 0:
+            gsess.prefill()
+        else:
+            gsess.refresh(b)
+        while not osess.block_done(b):
+            s0, s1 = osess.block_span(b)
+            before = osess.tokens[:, s0:s1].copy()
+            gsess.tokens.copy_(torch.from_numpy(osess.tokens.astype(np.int32)))
+            g = gsess.step(b)
+            o = osess.step(b)
+            torch.cuda.synchronize()
+            gl = g["logits"].cpu().numpy().reshape(o["logits"].shape).astype(np.float64)
+            err = rel_inf(gl, o["logits"])
+            worst = max(worst, err)
+            assert err < logits_tol, f"block {b}: logits rel err {err}"
+            gconf = g["conf"].cpu().numpy().astype(np.float64)
+            garg = g["argmax"].cpu().numpy()
+            gtok = gsess.tokens.cpu().numpy()[:, s0:s1]
+            masked = before == m.mask_id
+            # per-row bound: |d log p_max| <= 2 max_v |d logit|, so a confidence c can move
+            # by at most c (exp(2 dl) - 1); fp32 configs use the 1e-3 margin as well
+            dl = np.max(np.abs(gl - o["logits"]), axis=-1)            # [B, K]
+            unc = o["conf"] * np.expm1(2.0 * dl) + 1e-6
+            if fp32_decisions:
+                unc = np.maximum(unc, 1e-3)
+            ok = safe_sequences(o["conf"], unc, wl.threshold, masked)
+            for bb in range(wl.batch):
+                for i in range(wl.block_len):
+                    z = np.sort(o["logits"][bb, i][np.arange(m.vocab) != m.mask_id])
+                    if z[-1] - z[-2] > 2.0 * dl[bb, i] + 1e-6:
+                        assert garg[bb, i] == o["argmax"][bb, i], f"block {b} seq {bb} row {i}"
+                if not ok[bb]:
+                    excluded += 1
+                    continue
+                checked += 1
+                assert np.array_equal(gtok[bb], osess.tokens[bb, s0:s1]), f"block {b} seq {bb}"
+                assert g["n_unmasked"][bb].item() == o["n_unmasked"][bb]
+                assert g["remaining"][bb].item() == o["remaining"][bb]
+            if fp32_decisions:
+                assert np.max(np.abs(gconf - o["conf"])) < 1e-4
+    return worst, checked, excluded
+
+
+@pytest.mark.parametrize("mode", ["dual", "prefix"])
+def test_tiny_fp32_teacher_forced(lib, mode):
+    wl = replace(synth.WORKLOADS["tiny_dual"], cache_mode=mode)
+    worst, checked, excluded = teacher_forced(lib, wl, 1e-4, True)
+    assert checked >= 0.8 * (checked + excluded)
+
+
+def test_tiny_fp32_free_running_generate(lib):
+    wl = synth.WORKLOADS["tiny_dual"]
+    M = om.OracleModel(wl)
+    prompt = synth.make_prompt(wl)
+    seen_margins = []
+    osess = OSession(M, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+
+    def rec(b, n, out):
+        s0, s1 = osess.block_span(b)
+        masked = (osess.tokens[:, s0:s1] == wl.model.mask_id) | out["U"]
+        seen_margins.append(decision_margin_ok(out["conf"], wl.threshold, masked)[0])
+    want, ost = osess.generate(on_step=rec)
+    gs = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, wl.threshold,
+                 wl.cache_mode)
+    got, gst = gs.generate()
+    assert gst["steps"] == sum(gst["steps_per_block"])
+    assert gst["refreshes"] == wl.gen_len // wl.block_len
+    if all(seen_margins):
+        assert np.array_equal(got, want)
+        assert gst["steps_per_block"] == ost["steps_per_block"]
+
+
+def small_bf16(Hq=2, Hkv=2, mode="dual", B=2, P=40, G=64, K=32, V=2048, gain=0.1, scale=12.0):
+    m = synth.ModelShape(n_layers=2, d_model=256, n_heads=Hq, n_kv_heads=Hkv, head_dim=128,
+                         d_ffn=512, vocab=V, logit_scale=scale, dtype="bf16")
+    return synth.Workload("small_bf16", m, batch=B, prompt_len=P, gen_len=G, block_len=K,
+                          cache_mode=mode, norm_gain_std=gain)
+
+
+@pytest.mark.parametrize("Hq,Hkv,mode,B,K", [(2, 2, "dual", 2, 32), (4, 1, "dual", 3, 16),
+                                           (2, 2, "prefix", 2, 32), (2, 1, "prefix", 1, 8)])
+def test_small_bf16_teacher_forced(lib, Hq, Hkv, mode, B, K):
+    wl = small_bf16(Hq, Hkv, mode, B=B, K=K)
+    worst, checked, excluded = teacher_forced(lib, wl, 2e-2, False)
+    print(f"worst logits rel err {worst:.2e}; sequences-steps checked {checked}, excluded {excluded}")
+    assert checked > 0
+
+
+def test_bf16_steps_are_deterministic(lib):
+    wl = small_bf16()
+    model = gpu_model(lib, wl)
+    prompt = synth.make_prompt(wl)
+    outs = []
+    for _ in range(2):
+        s = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+        s.prefill()
+        o = s.step(0)
+        torch.cuda.synchronize()
+        outs.append((o["logits"].cpu().numpy().copy(), s.tokens.cpu().numpy().copy()))
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_first_step_after_refresh_matches_full_forward_bf16(lib):
+    """Property (a) on the GPU path: after a refresh, the first cached step's logits equal
+    the oracle's no-cache full forward of the same tokens (both cache modes)."""
+    for mode in ("dual", "prefix"):
+        wl = small_bf16(mode=mode)
+        M = om.OracleModel(wl)
+        prompt = synth.make_prompt(wl)
+        gs = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, wl.threshold, mode)
+        gs.prefill()
+        o = gs.step(0)
+        torch.cuda.synchronize()
+        toks = np.concatenate([prompt, np.full((wl.batch, wl.gen_len), wl.model.mask_id)], 1)
+        s0 = wl.prompt_len
+        _, ref = om.full_forward(M, toks, logit_rows=slice(s0, s0 + wl.block_len))
+        got = o["logits"].cpu().numpy().reshape(ref.shape)
+        assert rel_inf(got, ref) < 2e-2
+
+
+def test_generate_properties_llada_shape_two_blocks(lib):
+    """The 8B LLaDA shape (weights made on the device), DualCache, 2 blocks of 32:
+    every step decodes >= 1 token, blocks finish in <= 32 steps, no mask token is
+    emitted, and two runs give identical tokens."""
+    wl = replace(synth.WORKLOADS["llada8b_dual_p1000_g1024"], gen_len=64)
+    wl = synth.with_scale(wl, 20.0)
+    model = Model.synthetic(lib, wl)
+    prompt = synth.make_prompt(wl)
+    res = []
+    for _ in range(2):
+        s = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+        toks, st = s.generate()
+        res.append(toks)
+        assert all(1 <= n <= 32 for n in st["steps_per_block"])
+        assert st["refreshes"] == 2
+        assert not (toks == wl.model.mask_id).any()
+        assert toks.min() >= 0 and toks.max() < wl.model.vocab - 1
+    assert np.array_equal(res[0], res[1])
+    del model
+    torch.cuda.empty_cache()
