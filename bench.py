@@ -167,6 +167,8 @@ def main():
     ap.add_argument("--gen-len", type=int, default=0, help="override (for quick runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--roofline-kernel", default="auto")
+    ap.add_argument("--logit-scale", type=float, default=0.0,
+                    help="override the calibrated scale (exploration only)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the multi-GPU "
@@ -178,7 +180,8 @@ def main():
     from diffusion_dllm_block_amd.engine import Model, Session
 
     lib = bd.load()
-    wl = synth.with_scale(synth.WORKLOADS[a.workload], logit_scale(a.workload))
+    wl = synth.with_scale(synth.WORKLOADS[a.workload],
+                          a.logit_scale if a.logit_scale else logit_scale(a.workload))
     if a.gen_len:
         wl = replace(wl, gen_len=a.gen_len)
     log(f"workload {wl.name}: B={wl.batch} P={wl.prompt_len} G={wl.gen_len} K={wl.block_len} "

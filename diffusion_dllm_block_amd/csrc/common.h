@@ -44,6 +44,12 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16: A lane l holds row l%16, k = 8(l/16)..+8; B lane l holds
+// column l%16, the same k; C lane l holds column l%16, rows 4(l/16)..+4.
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8, v);
 }
@@ -58,23 +64,41 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Device-scope "last block" detection for fixed-order split reductions.  Every
-// workgroup of a group calls it once after writing its partial results; exactly one
-// (the last to arrive) gets true, after which it may read all partials.  The counter
-// is reset to 0 by that workgroup, so it is clean for the next launch.
+// Cross-workgroup hand-off of split partial results without cache-wide maintenance.
+// Partials are written with device-coherent stores (relaxed agent-scope atomics: the
+// store carries sc1 and is acknowledged once it is visible to every XCD) and read back
+// with device-coherent loads.  A device-scope release/acquire fence would instead write
+// back and invalidate the whole L2 of the issuing XCD on every arrival.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_dev(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// "Last block" detection for fixed-order split reductions.  Every workgroup of a group
+// calls it once after publishing its partials with st_dev; exactly one (the last to
+// arrive) gets true and may then read all partials with ld_dev.  The wait makes each
+// thread's coherent stores complete before the barrier, hence before the arrival
+// counter moves.  The counter is reset by the last workgroup, so it is clean for the
+// next launch.
 __device__ __forceinline__ bool arrive_last(int* counter, int expected, int* lds_flag) {
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    int prev = atomicAdd(counter, 1);
+    int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int last = (prev == expected - 1);
-    if (last) atomicExch(counter, 0);
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last;
   }
   __syncthreads();
-  bool last = *lds_flag != 0;
-  if (last) __threadfence();
-  return last;
+  return *lds_flag != 0;
 }
 
 }  // namespace dllm

@@ -37,106 +37,134 @@ __device__ __forceinline__ bf16x8 pack_p(const float* p, int u) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// 4 bf16 at keys k..k+3 (k % 4 == 0) of a Vt row of stride Sp (Sp % 8 == 0, Sp >= S);
+// keys >= S read as zero.  Branch-free: the address is clamped inside the row and the
+// value masked, so the padding past S (never written) cannot leak in.
+__device__ __forceinline__ uint64_t load4_masked(const uint16_t* row, int k, int S, int Sp) {
+  const uint64_t v = *reinterpret_cast<const uint64_t*>(row + min(k, Sp - 4));
+  const int n = S - k;
+  const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : (1ull << (16 * n)) - 1ull);
+  return v & keep;
+}
+
 // Vt operand for keys {16u + 4g + 0..3, 16u + 8 + 4g + 0..3} of a 32-key tile at key0,
 // row d; keys >= S read as zero.
-__device__ __forceinline__ bf16x8 load_vt(const uint16_t* vrow, int key0, int u, int g, int S) {
-  int ka = key0 + 16 * u + 4 * g;
-  int kb = ka + 8;
-  u32x2 a = u32x2{}, b = u32x2{};
-  if (ka < S) a = *reinterpret_cast<const u32x2*>(vrow + ka);
-  if (kb < S) b = *reinterpret_cast<const u32x2*>(vrow + kb);
-  if (ka + 4 > S) {  // partial run at the end of the sequence
-    uint16_t* pa = reinterpret_cast<uint16_t*>(&a);
-    for (int e = 0; e < 4; ++e) if (ka + e >= S) pa[e] = 0;
-  }
-  if (kb + 4 > S) {
-    uint16_t* pb = reinterpret_cast<uint16_t*>(&b);
-    for (int e = 0; e < 4; ++e) if (kb + e >= S) pb[e] = 0;
-  }
-  u32x4 r = u32x4{a.x, a.y, b.x, b.y};
+__device__ __forceinline__ bf16x8 load_vt(const uint16_t* vrow, int key0, int u, int g, int S,
+                                          int Sp) {
+  const int ka = key0 + 16 * u + 4 * g;
+  const uint64_t a = load4_masked(vrow, ka, S, Sp);
+  const uint64_t b = load4_masked(vrow, ka + 8, S, Sp);
+  u32x4 r = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
   return as_bf16x8(r);
 }
 
 // ============================================================================
 // Split-KV attention for a few query rows (a block step): grid (nchunk, Hq*nqt, B),
-// 4 waves; wave w covers keys chunk*128 + w*32 .. +32 for a tile of 32 query rows.
+// 4 waves.  Chunk c covers keys [c*4*kpw, (c+1)*4*kpw); wave w walks its kpw keys in
+// 32-key sub-tiles with an online softmax, loading the next sub-tile's K and Vt while
+// the current one is in the MFMAs.  The 4 waves are merged in LDS; with several chunks
+// the workgroup writes unnormalised partials (O, m, l) and attn_combine merges them.
 // ============================================================================
-__global__ __launch_bounds__(256, 2) void attn_splitkv_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
-    int Sp, int nqt, int nchunk, float scale_log2, float* part_o, float* part_ml,
-    int* counters) {
-  __shared__ float red_m[4][32], red_l[4][32];
-  __shared__ float osum[HD][33];
-  __shared__ int flag;
-  const int chunk = blockIdx.x;
-  const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
-  const int hkv = hq / (Hq / Hkv);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 31, g = l >> 5;
-  const int key0 = chunk * 128 + w * 32;
+struct KVTile {
+  u32x4 k[8];       // K operand: key lr, d = 16t + 8g .. +8
+  bf16x8 v[4][2];   // Vt operands: d = 32dt + lr, keys of accumulator rows 8u .. 8u+7
+};
 
-  // Q^T operand: lane (query lr, half g) holds Q[row][16t + 8g .. +8]
-  const int qrow = qt * 32 + lr;
-  const uint16_t* qp = q + (((int64_t)b * Hq + hq) * R + qrow) * HD + 8 * g;
-  u32x4 qf[8];
+__device__ __forceinline__ void load_kv_tile(KVTile& t, const uint16_t* kbase,
+                                             const uint16_t* vbase, int key0, int lr, int g,
+                                             int S, int Sp) {
+  // keys >= S: any valid K row will do (their scores are masked to -inf)
+  const int key = min(key0 + lr, S - 1);
+  const uint16_t* kp = kbase + (int64_t)key * HD + 8 * g;
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-    qf[t] = (qrow < R) ? *reinterpret_cast<const u32x4*>(qp + 16 * t) : u32x4{};
-  // K operand: lane (key lr, half g)
-  const int key = key0 + lr;
-  const uint16_t* kp = k + (((int64_t)b * Hkv + hkv) * Sp + key) * HD + 8 * g;
-  u32x4 kf[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-    kf[t] = (key < S) ? *reinterpret_cast<const u32x4*>(kp + 16 * t) : u32x4{};
-  // Vt operands: rows d = 32*dt + lr
-  const uint16_t* vbase = vt + ((int64_t)b * Hkv + hkv) * HD * Sp;
-  bf16x8 vf[4][2];
+  for (int i = 0; i < 8; ++i) t.k[i] = *reinterpret_cast<const u32x4*>(kp + 16 * i);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      vf[dt][u] = load_vt(vbase + (int64_t)(32 * dt + lr) * Sp, key0, u, g, S);
+      t.v[dt][u] = load_vt(vbase + (int64_t)(32 * dt + lr) * Sp, key0, u, g, S, Sp);
+}
 
-  f32x16 s = {};
-#pragma unroll
-  for (int t = 0; t < 8; ++t) s = mfma32(as_bf16x8(kf[t]), as_bf16x8(qf[t]), s);
+__global__ __launch_bounds__(256) void attn_splitkv_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
+    int Sp, int nqt, int nchunk, int nsub, float scale_log2, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  __shared__ float red_m[4][32], red_l[4][32];
+  __shared__ float osum[HD][33];
+  const int chunk = blockIdx.x;
+  const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
+  const int hkv = hq / (Hq / Hkv);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 31, g = l >> 5;
+  const int kpw = 32 * nsub;
+  const int wkey0 = chunk * 4 * kpw + w * kpw;
 
-  float p[16];
-  float mx = -INFINITY;
+  // Q^T operand: lane (query lr, half g) holds Q[row][16t + 8g .. +8]
+  const int qrow = min(qt * 32 + lr, R - 1);  // rows >= R: computed, never stored
+  const uint16_t* qp = q + (((int64_t)b * Hq + hq) * R + qrow) * HD + 8 * g;
+  u32x4 qf[8];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = (key0 + acc_row(v, g) < S) ? s[v] * scale_log2 : -INFINITY;
-    p[v] = x;
-    mx = fmaxf(mx, x);
-  }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-  const float ms = (mx == -INFINITY) ? 0.f : mx;
-  float ls = 0.f;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    p[v] = __builtin_amdgcn_exp2f(p[v] - ms);
-    ls += p[v];
-  }
-  ls += __shfl_xor(ls, 32, kWave);
+  for (int t = 0; t < 8; ++t) qf[t] = *reinterpret_cast<const u32x4*>(qp + 16 * t);
+  const uint16_t* kbase = k + ((int64_t)b * Hkv + hkv) * Sp * HD;
+  const uint16_t* vbase = vt + ((int64_t)b * Hkv + hkv) * HD * Sp;
 
   f32x16 oacc[4];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    oacc[dt] = f32x16{};
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  auto consume = [&](const KVTile& t, int key0) {
+    f32x16 s = {};
 #pragma unroll
-    for (int u = 0; u < 2; ++u) oacc[dt] = mfma32(vf[dt][u], pack_p(p, u), oacc[dt]);
+    for (int i = 0; i < 8; ++i) s = mfma32(as_bf16x8(t.k[i]), as_bf16x8(qf[i]), s);
+    float p[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = (key0 + acc_row(v, g) < S) ? s[v] * scale_log2 : -INFINITY;
+      p[v] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    if (m_new == -INFINITY) return;  // no valid key yet for this wave
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      p[v] = __builtin_amdgcn_exp2f(p[v] - m_new);
+      ls += p[v];
+    }
+    ls += __shfl_xor(ls, 32, kWave);
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      oacc[dt] *= alpha;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) oacc[dt] = mfma32(t.v[dt][u], pack_p(p, u), oacc[dt]);
+    }
+  };
+
+  KVTile ta, tb;
+  load_kv_tile(ta, kbase, vbase, wkey0, lr, g, S, Sp);
+  for (int j = 0; j < nsub; j += 2) {
+    if (j + 1 < nsub) load_kv_tile(tb, kbase, vbase, wkey0 + 32 * (j + 1), lr, g, S, Sp);
+    consume(ta, wkey0 + 32 * j);
+    if (j + 1 >= nsub) break;
+    if (j + 2 < nsub) load_kv_tile(ta, kbase, vbase, wkey0 + 32 * (j + 2), lr, g, S, Sp);
+    consume(tb, wkey0 + 32 * (j + 1));
   }
 
   // ---- merge the 4 waves (fixed order)
-  if (g == 0) { red_m[w][lr] = mx; red_l[w][lr] = ls; }
+  if (g == 0) { red_m[w][lr] = m_run; red_l[w][lr] = l_run; }
   __syncthreads();
   float M = red_m[0][lr];
   for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i][lr]);
   float L = 0.f;
   for (int i = 0; i < 4; ++i)
     L += (red_m[i][lr] == -INFINITY) ? 0.f : red_l[i][lr] * __builtin_amdgcn_exp2f(red_m[i][lr] - M);
-  const float f = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mx - M);
+  const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
   for (int ww = 0; ww < 4; ++ww) {
     if (w == ww) {
 #pragma unroll
@@ -150,12 +178,11 @@ __global__ __launch_bounds__(256, 2) void attn_splitkv_bf16(
     }
     __syncthreads();
   }
+  // L and M per query are identical in every wave; publish them through LDS
+  if (w == 0 && g == 0) { red_m[0][lr] = M; red_l[0][lr] = L; }
+  __syncthreads();
 
-  const int64_t grp = ((int64_t)b * Hq + hq) * nqt + qt;
   if (nchunk == 1) {
-    // L per query lives in lanes; publish it through LDS (all reads of red_l are done)
-    if (w == 0 && g == 0) red_l[0][lr] = L;
-    __syncthreads();
     for (int e = threadIdx.x; e < 32 * HD; e += blockDim.x) {
       int qi = e / HD, d = e % HD;
       int row = qt * 32 + qi;
@@ -164,35 +191,67 @@ __global__ __launch_bounds__(256, 2) void attn_splitkv_bf16(
     }
     return;
   }
-
-  // ---- publish this chunk's partial (m, l, O) and let the last chunk combine
+  const int64_t grp = ((int64_t)b * Hq + hq) * nqt + qt;
   float* po = part_o + (grp * nchunk + chunk) * (32 * HD);
-  for (int e = threadIdx.x; e < 32 * HD; e += blockDim.x) {
-    int qi = e / HD, d = e % HD;
-    po[e] = osum[d][qi];
-  }
-  if (w == 0 && g == 0) {
+  for (int e = threadIdx.x; e < 32 * HD; e += blockDim.x) po[e] = osum[e % HD][e / HD];
+  if (threadIdx.x < 64) {
     float* pml = part_ml + (grp * nchunk + chunk) * 64;
-    pml[lr] = M;
-    pml[32 + lr] = L;
+    pml[threadIdx.x] = threadIdx.x < 32 ? red_m[0][threadIdx.x] : red_l[0][threadIdx.x - 32];
   }
-  if (!arrive_last(&counters[grp], nchunk, &flag)) return;
+}
 
-  // combine chunks in order; thread handles query qi = e / HD for its elements
-  for (int e = threadIdx.x; e < 32 * HD; e += blockDim.x) {
-    int qi = e / HD, d = e % HD;
-    int row = qt * 32 + qi;
-    if (row >= R) continue;
-    const float* pml = part_ml + grp * nchunk * 64;
-    float Mx = -INFINITY;
-    for (int c = 0; c < nchunk; ++c) Mx = fmaxf(Mx, pml[c * 64 + qi]);
-    float Ls = 0.f, acc = 0.f;
+// Merge the chunk partials: o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, chunks in
+// order.  grid (B*Hq*nqt, 4): workgroup y handles 8 query rows of the 32-row tile.
+constexpr int kMaxChunks = 64;
+__global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ part_o,
+                                                    const float* __restrict__ part_ml,
+                                                    uint16_t* __restrict__ o, int Hq, int R,
+                                                    int nqt, int nchunk) {
+  __shared__ float wts[kMaxChunks][8];
+  const int64_t grp = blockIdx.x;
+  const int qt = (int)(grp % nqt);
+  const int hq = (int)((grp / nqt) % Hq);
+  const int b = (int)(grp / ((int64_t)nqt * Hq));
+  const int q0 = blockIdx.y * 8;
+  const float* pml = part_ml + grp * nchunk * 64;
+  if (threadIdx.x < 8) {
+    const int qi = q0 + threadIdx.x;
+    float M = -INFINITY;
+    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, pml[c * 64 + qi]);
+    float L = 0.f;
     for (int c = 0; c < nchunk; ++c) {
-      float fc = __builtin_amdgcn_exp2f(pml[c * 64 + qi] - Mx);
-      Ls += pml[c * 64 + 32 + qi] * fc;
-      acc += part_o[(grp * nchunk + c) * (32 * HD) + e] * fc;
+      float mc = pml[c * 64 + qi];
+      float f = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+      wts[c][threadIdx.x] = f;
+      L += pml[c * 64 + 32 + qi] * f;
     }
-    o[((int64_t)b * R + row) * (Hq * HD) + hq * HD + d] = f2bf(acc / Ls);
+    const float inv = 1.0f / L;
+    for (int c = 0; c < nchunk; ++c) wts[c][threadIdx.x] *= inv;
+  }
+  __syncthreads();
+  // thread -> (query q0 + tid/32, dims 4*(tid%32) .. +4)
+  const int qi = threadIdx.x >> 5, d4 = (threadIdx.x & 31) * 4;
+  const int row = qt * 32 + q0 + qi;
+  const float* pb = part_o + grp * nchunk * (32 * HD) + (q0 + qi) * HD + d4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < nchunk; c0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = (c0 + u < nchunk) ? *reinterpret_cast<const float4*>(pb + (int64_t)(c0 + u) * 32 * HD)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u < nchunk) {
+        const float wgt = wts[c0 + u][qi];
+        acc.x += v[u].x * wgt; acc.y += v[u].y * wgt; acc.z += v[u].z * wgt; acc.w += v[u].w * wgt;
+      }
+    }
+  }
+  if (row < R) {
+    u16x4 r;
+    r[0] = f2bf(acc.x); r[1] = f2bf(acc.y); r[2] = f2bf(acc.z); r[3] = f2bf(acc.w);
+    *reinterpret_cast<u16x4*>(o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD + d4) = r;
   }
 }
 
@@ -381,11 +440,19 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
   if (R <= 64) {
     p.kind = 1;
     p.nqt = (R + 31) / 32;
-    p.nchunk = (S + 127) / 128;
-    if (p.nchunk > 1) {
-      p.part_floats = (size_t)B * Hq * p.nqt * p.nchunk * (32 * HD + 64);
-      p.counters = B * Hq * p.nqt;
+    const int base = B * Hq * p.nqt;
+    int target = (512 + base - 1) / base;          // chunks wanted for ~512 workgroups
+    if (target < 1) target = 1;
+    int ck = (S + target - 1) / target;             // keys per chunk
+    ck = (ck + 127) / 128 * 128;                    // 4 waves x 32-key sub-tiles
+    int nchunk = (S + ck - 1) / ck;
+    if (nchunk > kMaxChunks) {
+      ck = ((S + kMaxChunks - 1) / kMaxChunks + 127) / 128 * 128;
+      nchunk = (S + ck - 1) / ck;
     }
+    p.nchunk = nchunk;
+    p.nsub = ck / 128;
+    if (p.nchunk > 1) p.part_floats = (size_t)base * p.nchunk * (32 * HD + 64);
   } else {
     p.kind = 2;
     p.nqt = (R + 127) / 128;
@@ -396,6 +463,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
 hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const void* k,
                             const void* vt, void* o, int B, int Hq, int Hkv, int R, int S, int Sp,
                             int D, float* part, int* counters, hipStream_t st) {
+  (void)counters;
   if (B <= 0 || R <= 0) return hipSuccess;
   if (p.kind == 0) {
     size_t sh = (size_t)(S + D) * sizeof(float);
@@ -406,11 +474,18 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
   }
   const float scale_log2 = kLog2e / sqrtf((float)D);
   if (p.kind == 1) {
+    const int64_t groups = (int64_t)B * Hq * p.nqt;
     float* part_o = part;
-    float* part_ml = part + (size_t)B * Hq * p.nqt * p.nchunk * (32 * HD);
+    float* part_ml = part ? part + groups * p.nchunk * (32 * HD) : nullptr;
     attn_splitkv_bf16<<<dim3(p.nchunk, Hq * p.nqt, B), 256, 0, st>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
-        S, Sp, p.nqt, p.nchunk, scale_log2, part_o, part_ml, counters);
+        S, Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part_o, part_ml);
+    if (p.nchunk > 1) {
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      attn_combine<<<dim3((unsigned)groups, 4), 256, 0, st>>>(part_o, part_ml, (uint16_t*)o, Hq,
+                                                              R, p.nqt, p.nchunk);
+    }
   } else {
     attn_flash_bf16<<<dim3(p.nqt, Hq, B), 256, 0, st>>>(
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,

@@ -131,9 +131,9 @@ __global__ __launch_bounds__(256) void conf_unmask_kernel(
     Trip a = red[0];
     for (int i = 1; i < (int)(blockDim.x / kWave); ++i) a = merge(a, red[i]);
     int64_t o = (int64_t)row * nsplit + split;
-    pm[o] = a.m;
-    ps[o] = a.s;
-    pi[o] = a.idx;
+    st_dev(&pm[o], a.m);
+    st_dev(&ps[o], a.s);
+    st_dev(&pi[o], a.idx);
   }
 
   const int b = row / K;
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256) void conf_unmask_kernel(
     Trip a{-INFINITY, 0.f, 0x7fffffff};
     for (int sp = 0; sp < nsplit; ++sp) {
       int64_t o = (int64_t)r * nsplit + sp;
-      Trip u{pm[o], ps[o], pi[o]};
+      Trip u{ld_dev(&pm[o]), ld_dev(&ps[o]), ld_dev(&pi[o])};
       a = merge(a, u);
     }
     c = 1.0f / a.s;

@@ -11,16 +11,15 @@
 //   RESID  : fp32 residual stream += tile;  F32: logits = logit_scale * tile;  STORE.
 //
 // Kernels:
-//   gemm_skinny_bf16 (M <= 64): weight streaming.  Each wave owns 32 weight rows and
-//     loads them straight from HBM into MFMA operand registers (16-byte loads, two
-//     register sets so the next 128-wide K stage is in flight during the current one);
-//     the activation slice is staged once per workgroup in LDS and shared by 4 waves.
-//     Split-K over gridDim.y fills the chip; partial tiles go to a workspace and the
-//     last workgroup of a tile (device-scope arrival counter) sums them in split order
-//     and runs the epilogue: deterministic, no float atomics.
+//   gemm_skinny_bf16 (M <= 64): weight streaming, 64-column tiles of 8 waves (see below).
+//     Residual GEMMs split K over gridDim.y and leave fp32 partials that the next
+//     RMSNorm adds into the residual stream in split order; the others split K only
+//     when the column tiles alone cannot fill the chip, and then the last workgroup of
+//     a tile (device-scope arrival counter) sums the partials in split order and runs
+//     the epilogue.  Deterministic either way: no float atomics.
 //   gemm_tiled_bf16 (M > 64): 128x128 output tiles, 64-wide K stages double-buffered in
 //     LDS with register prefetch, 4 waves each computing 64x64 with 32x32x16 MFMAs; the
-//     same split-K machinery for shapes with too few tiles.
+//     same split-K schemes for shapes with too few tiles.
 //   gemm_f32: SIMT fp32 kernel for fp32 models (32x128 tiles).
 #include "common.h"
 #include "kernels.h"
@@ -100,128 +99,179 @@ __device__ void epilogue(const float* tile, int ldt, int rows, int m0, int vc0, 
   }
 }
 
-// Sum split-K partials [splits][M][Nv] of one tile in split order into the LDS tile.
+// Sum of `splits` device-coherent partials p[0], p[stride], ... in split order; the
+// loads of a group of 8 are issued together.
+__device__ __forceinline__ float sum_splits(const float* p, int64_t stride, int splits) {
+  float s = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (s0 + u < splits) ? ld_dev(p + (s0 + u) * stride) : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  return s;
+}
+
+// Sum split-K partials [splits][M][Nv] of one 128-column tile in split order into LDS.
 __device__ __forceinline__ void gather_partials(float* tile, int ldt, int rows, int m0, int vc0,
                                                 int M, int Nv, int splits, const float* part) {
   for (int i = threadIdx.x; i < rows * 128; i += blockDim.x) {
     int r = i >> 7, c = i & 127;
     int m = m0 + r, vc = vc0 + c;
-    float s = 0.f;
-    if (m < M && vc < Nv)
-      for (int sp = 0; sp < splits; ++sp) s += part[((int64_t)sp * M + m) * Nv + vc];
-    tile[r * ldt + c] = s;
+    tile[r * ldt + c] = (m < M && vc < Nv)
+        ? sum_splits(part + (int64_t)m * Nv + vc, (int64_t)M * Nv, splits) : 0.f;
   }
 }
 
 // ============================================================================
-// skinny bf16 GEMM
+// skinny bf16 GEMM (M <= 64): weight streaming
 // ============================================================================
-constexpr int SK_KS = 128;          // K per stage
-constexpr int SK_LDX = SK_KS + 8;   // LDS row stride of the activation stage (elements)
-constexpr int TL = 132;             // LDS row stride of the fp32 epilogue tile
+// Workgroup = 8 waves over a tile of 64 virtual columns and a K range of 1024 (512 when
+// M > 32): wave w owns columns 16*(w&3)..+16 and the (w>>2)-th half of the K range.
+// The activation slice X[M][K range] is loaded once into LDS; each wave issues all of
+// its weight loads (16 x 16 bytes per lane, straight into 16x16x32 MFMA operand
+// registers) before its first MFMA, so there is no per-stage barrier and the whole
+// slice of W is in flight at once.  The two K halves are summed in LDS; K ranges are
+// combined across workgroups as described for the split-K schemes above.
+constexpr int S2_NT = 64;          // virtual columns per workgroup
+constexpr int S2_TL = S2_NT + 4;   // LDS row stride of the fp32 result tile
 
-template <int EPI, int MT>
-__global__ __launch_bounds__(256, 2) void gemm_skinny_bf16(
+// virtual column -> weight row for 64-column tiles:
+//   SWIGLU: tile t = gate rows 32t..+32 then up rows F+32t..+32;
+//   QKV (head_dim 128): tile t = head t/2, dims 32(t&1)..+32 then the same dims + 64,
+//   so RoPE pairs (d, d+64) sit in one tile.
+template <int EPI>
+__device__ __forceinline__ int wrow_s2(int vc, int F) {
+  const int t = vc >> 6, c = vc & 63;
+  if constexpr (EPI == EPI_SWIGLU) {
+    return c < 32 ? t * 32 + c : F + t * 32 + (c - 32);
+  } else if constexpr (EPI == EPI_QKV) {
+    const int hs = t >> 1, part = t & 1;
+    return hs * 128 + (c < 32 ? part * 32 + c : 64 + part * 32 + (c - 32));
+  } else {
+    return vc;
+  }
+}
+
+// Tiles of 64 virtual columns.  Workgroup = 8 waves: wave w owns columns 16*(w&3)..+16 and
+// the (w>>2)-th half of the workgroup's K range (KR).  XV = 16-byte activation loads per
+// thread to fill the LDS slice; NLOAD = weight loads per lane per tile.
+template <int MT, int KR> struct SkinnyCfg {
+  static constexpr int KW = KR / 2;
+  static constexpr int NLOAD = KW / 32;
+  static constexpr int LDX = KR + 8;                 // LDS row stride (elements)
+  static constexpr int XV = MT * 16 * KR / 8 / 512;
+  static_assert(XV >= 1, "activation slice smaller than one load per thread");
+};
+
+// Persistent weight-streaming GEMM for M <= 64 rows.
+//   * The grid holds one workgroup per CU; a workgroup is pinned to one K range
+//     (blockIdx % splits) and walks the column tiles tn = wid, wid + nw, ...
+//   * Its activation slice X[M][KR] is loaded into LDS once.
+//   * Each lane keeps NLOAD weight loads in flight: register t is refilled with the next
+//     tile's weights right after the MFMAs of step t consumed it, so the weight stream
+//     does not pause between tiles.  After the last tile the refills read a fixed cached
+//     line instead of branching, and every tile writes its split partials through
+//     unconditional stores (out-of-range lanes write a trash slot): the loop has no
+//     data-dependent branches, which keeps the compiler's wait counts exact.
+//   * Partials [split][M][Nv] (virtual column order) are summed in split order by
+//     reduce_epilogue, or for the residual GEMMs by the next RMSNorm.
+template <int MAP, int MT, int KR>
+__global__ __launch_bounds__(512, 1) void gemm_skinny_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv,
-    int K, int kchunk, int splits, float* part, int* counters, EpiArgs e) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[2][MT * 32 * SK_LDX];
-  __shared__ float tile[MT * 32 * TL];
-  __shared__ int flag;
-  const int tn = blockIdx.x, split = blockIdx.y;
+    int K, int F, int splits, int ntn, float* __restrict__ part, float* __restrict__ trash) {
+  using C = SkinnyCfg<MT, KR>;
+  __shared__ __attribute__((aligned(16))) uint16_t Xs[MT * 16 * C::LDX];
+  __shared__ float red[MT * 16 * S2_TL];
+  const int split = blockIdx.x % splits;
+  const int wid = blockIdx.x / splits;
+  const int nw = gridDim.x / splits;  // workgroups per K range (grid is a multiple of splits)
+  if (wid >= ntn) return;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lr = l & 31, g = l >> 5;
-  const int vc = tn * 128 + w * 32 + lr;
-  const bool wv = vc < Nv;
-  const int wrow = wv ? wrow_of<EPI>(vc, e.F) : 0;
-  const int kb = split * kchunk;
-  const int ke = min(K, kb + kchunk);
-  const int nst = (ke - kb) / SK_KS;
-  const uint16_t* wp = W + (int64_t)wrow * K + kb + 8 * g;
-  const uint16_t* xp = X + kb;
+  const int w = tid >> 6, ng = w & 3, kg = w >> 2, l = tid & 63, ln = l & 15, g = l >> 4;
+  const int kb = split * KR;
 
-  constexpr int XV = MT * 2;  // 16-byte activation vectors per thread per stage
-  u32x4 xr[XV];
-  u32x4 wa[8], wb[8];
-  f32x16 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
+  auto wptr = [&](int tn) {  // columns past Nv read a clamped valid row (never stored)
+    const int vc = min(tn * S2_NT + ng * 16 + ln, Nv - 1);
+    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + kb + kg * C::KW + 8 * g;
+  };
 
-  auto load_x = [&](int st) {
+  {  // activation slice -> LDS (rows >= M read row M-1; never stored)
+    u32x4 xr[C::XV];
 #pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      int ee = tid + 256 * i;
-      int r = ee >> 4, c8 = ee & 15;
-      xr[i] = (r < M) ? *reinterpret_cast<const u32x4*>(xp + (int64_t)r * ldx + st * SK_KS + 8 * c8)
-                      : u32x4{};
+    for (int i = 0; i < C::XV; ++i) {
+      const int ee = tid + 512 * i;
+      const int r = ee / (KR / 8), c8 = ee % (KR / 8);
+      xr[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(r, M - 1) * ldx + kb + 8 * c8);
     }
-  };
-  auto store_x = [&](uint16_t* xs) {
 #pragma unroll
-    for (int i = 0; i < XV; ++i) {
-      int ee = tid + 256 * i;
-      int r = ee >> 4, c8 = ee & 15;
-      *reinterpret_cast<u32x4*>(&xs[r * SK_LDX + 8 * c8]) = xr[i];
+    for (int i = 0; i < C::XV; ++i) {
+      const int ee = tid + 512 * i;
+      const int r = ee / (KR / 8), c8 = ee % (KR / 8);
+      *reinterpret_cast<u32x4*>(&Xs[r * C::LDX + 8 * c8]) = xr[i];
     }
-  };
-  auto load_w = [&](u32x4* wr, int st) {
+  }
+  u32x4 wr[C::NLOAD];
+  {
+    const uint16_t* wp = wptr(wid);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      wr[t] = wv ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + st * SK_KS + 16 * t))
-                 : u32x4{};
-  };
-  auto compute = [&](const u32x4* wr, const uint16_t* xs) {
+    for (int t = 0; t < C::NLOAD; ++t)
+      wr[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + 32 * t));
+  }
+  __syncthreads();
+
+  for (int tn = wid; tn < ntn; tn += nw) {
+    const bool has_next = tn + nw < ntn;
+    // refill source: the next tile, or (after the last tile) one fixed line, step 0
+    const uint16_t* wpn = has_next ? wptr(tn + nw) : W;
+    const int tstride = has_next ? 32 : 0;
+    f32x4 acc[MT];
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
+#pragma unroll
+    for (int t = 0; t < C::NLOAD; ++t) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        u32x4 a = *reinterpret_cast<const u32x4*>(&xs[(mt * 32 + lr) * SK_LDX + 16 * t + 8 * g]);
-        acc[mt] = mfma32(as_bf16x8(a), as_bf16x8(wr[t]), acc[mt]);
+        u32x4 a = *reinterpret_cast<const u32x4*>(
+            &Xs[(mt * 16 + ln) * C::LDX + kg * C::KW + 32 * t + 8 * g]);
+        acc[mt] = mfma16(as_bf16x8(a), as_bf16x8(wr[t]), acc[mt]);
       }
-  };
+      wr[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wpn + tstride * t));
+    }
 
-  load_w(wa, 0);
-  load_x(0);
-  store_x(Xs[0]);
-  __syncthreads();
-  for (int st = 0; st < nst; st += 2) {
-    if (st + 1 < nst) { load_w(wb, st + 1); load_x(st + 1); }
-    compute(wa, Xs[0]);
-    if (st + 1 < nst) store_x(Xs[1]);
+    // sum the two K halves: red[m][c], c = 16*ng + column-in-MFMA
+    if (kg == 1) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(mt * 16 + 4 * g + r) * S2_TL + ng * 16 + ln] = acc[mt][r];
+    }
     __syncthreads();
-    if (st + 1 >= nst) break;
-    if (st + 2 < nst) { load_w(wa, st + 2); load_x(st + 2); }
-    compute(wb, Xs[1]);
-    if (st + 2 < nst) store_x(Xs[0]);
+    if (kg == 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[(mt * 16 + 4 * g + r) * S2_TL + ng * 16 + ln] += acc[mt][r];
+    }
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < MT * 16 * S2_NT / 512; ++i) {
+      const int idx = tid + 512 * i;
+      const int r = idx >> 6, c = idx & 63;
+      const int vcc = tn * S2_NT + c;
+      const bool ok = (r < M) && (vcc < Nv);
+      float* dst = ok ? part + ((int64_t)split * M + r) * Nv + vcc : trash + l;
+      *dst = red[r * S2_TL + c];
+    }
+    __syncthreads();  // red is reused by the next tile
   }
-
-  if (splits == 1) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) tile[(mt * 32 + acc_row(v, g)) * TL + w * 32 + lr] = acc[mt][v];
-    __syncthreads();
-    epilogue<uint16_t, EPI>(tile, TL, MT * 32, 0, tn * 128, M, Nv, e);
-    return;
-  }
-  if (wv) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        int m = mt * 32 + acc_row(v, g);
-        if (m < M) part[((int64_t)split * M + m) * Nv + vc] = acc[mt][v];
-      }
-  }
-  if (!arrive_last(&counters[tn], splits, &flag)) return;
-  gather_partials(tile, TL, MT * 32, 0, tn * 128, M, Nv, splits, part);
-  __syncthreads();
-  epilogue<uint16_t, EPI>(tile, TL, MT * 32, 0, tn * 128, M, Nv, e);
 }
 
 // ============================================================================
 // tiled bf16 GEMM
 // ============================================================================
+constexpr int TL = 132;  // LDS row stride of the fp32 128-column epilogue tile
 constexpr int TB_K = 64;
 constexpr int TB_LD = TB_K + 8;
 constexpr int TB_AB_BYTES = 2 * 2 * 128 * TB_LD * 2;
@@ -246,25 +296,24 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
   const int nst = (ke - kb) / TB_K;
 
   // loader: element e = tid + 256 i  ->  row e >> 3, 16-byte column e & 7
+  // rows past M / columns past Nv load from a clamped valid address; their results are
+  // discarded by the epilogue (unconditional loads keep the load counting exact)
   const uint16_t* arow[4];
   const uint16_t* brow[4];
-  bool av[4], bv[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     int ee = tid + 256 * i;
     int r = ee >> 3, c8 = ee & 7;
-    int m = m0 + r, vc = vc0 + r;
-    av[i] = m < M;
-    bv[i] = vc < Nv;
-    arow[i] = X + (int64_t)(av[i] ? m : 0) * ldx + kb + 8 * c8;
-    brow[i] = W + (int64_t)(bv[i] ? wrow_of<EPI>(vc, e.F) : 0) * K + kb + 8 * c8;
+    int m = min(m0 + r, M - 1), vc = min(vc0 + r, Nv - 1);
+    arow[i] = X + (int64_t)m * ldx + kb + 8 * c8;
+    brow[i] = W + (int64_t)wrow_of<EPI>(vc, e.F) * K + kb + 8 * c8;
   }
   u32x4 ra[4], rb[4];
   auto load = [&](int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = av[i] ? *reinterpret_cast<const u32x4*>(arow[i] + st * TB_K) : u32x4{};
-      rb[i] = bv[i] ? *reinterpret_cast<const u32x4*>(brow[i] + st * TB_K) : u32x4{};
+      ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + st * TB_K);
+      rb[i] = *reinterpret_cast<const u32x4*>(brow[i] + st * TB_K);
     }
   };
   auto store = [&](int buf) {
@@ -320,10 +369,19 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
     epilogue<uint16_t, EPI>(tile, TL, 128, m0, vc0, M, Nv, e);
     return;
   }
+  if constexpr (EPI == EPI_RESID) {
+    // deferred: the consumer of the residual stream sums the split partials in order
+    for (int i = tid; i < 128 * 128; i += 256) {
+      int r = i >> 7, c = i & 127;
+      int m = m0 + r, vc = vc0 + c;
+      if (m < M && vc < Nv) part[((int64_t)split * M + m) * Nv + vc] = tile[r * TL + c];
+    }
+    return;
+  }
   for (int i = tid; i < 128 * 128; i += 256) {
     int r = i >> 7, c = i & 127;
     int m = m0 + r, vc = vc0 + c;
-    if (m < M && vc < Nv) part[((int64_t)split * M + m) * Nv + vc] = tile[r * TL + c];
+    if (m < M && vc < Nv) st_dev(&part[((int64_t)split * M + m) * Nv + vc], tile[r * TL + c]);
   }
   if (!arrive_last(&counters[tm * gridDim.x + tn], splits, &flag)) return;
   gather_partials(tile, TL, 128, m0, vc0, M, Nv, splits, part);
@@ -382,30 +440,139 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int
 }
 
 // ============================================================================
+// split-K reduction + epilogue for the skinny GEMM (partials in 64-column virtual order)
+// ============================================================================
+// One thread per 4 consecutive outputs; partials summed in split order.
+__device__ __forceinline__ float4 sum_split4(const float* p, int64_t stride, int splits) {
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < splits; s0 += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = (s0 + u < splits) ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
+                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < splits) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+  }
+  return s;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void reduce_epilogue(const float* __restrict__ part, int splits,
+                                                       int M, int Nv, EpiArgs e) {
+  const int64_t stride = (int64_t)M * Nv;
+  const int64_t i4 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
+  if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
+    // Nv % 4 == 0: 4 outputs of one row
+    if (i4 >= stride) return;
+    const int m = (int)(i4 / Nv), vc = (int)(i4 % Nv);
+    float4 v = sum_split4(part + i4, stride, splits);
+    if constexpr (EPI == EPI_F32) {
+      float4 o = make_float4(v.x * e.scale, v.y * e.scale, v.z * e.scale, v.w * e.scale);
+      *reinterpret_cast<float4*>((float*)e.y + (int64_t)m * e.ldy + vc) = o;
+    } else {
+      uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.ldy + vc;
+      y[0] = f2bf(v.x); y[1] = f2bf(v.y); y[2] = f2bf(v.z); y[3] = f2bf(v.w);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // output column c of row m: gate at virtual column 64(c/32) + c%32, up 32 further
+    const int64_t nout = (int64_t)M * e.F;
+    if (i4 >= nout) return;
+    const int m = (int)(i4 / e.F), c = (int)(i4 % e.F);
+    const int vg = 64 * (c >> 5) + (c & 31);
+    const float* pr = part + (int64_t)m * Nv;
+    float4 gt = sum_split4(pr + vg, stride, splits);
+    float4 up = sum_split4(pr + vg + 32, stride, splits);
+    uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.F + c;
+    y[0] = f2bf(silu(gt.x) * up.x); y[1] = f2bf(silu(gt.y) * up.y);
+    y[2] = f2bf(silu(gt.z) * up.z); y[3] = f2bf(silu(gt.w) * up.w);
+  } else if constexpr (EPI == EPI_QKV) {
+    // (row m, head slot hs, dims d..d+3 < 64) -> pairs (d, d+64); head_dim 128
+    const int nslot = Nv / 128;
+    const int64_t nwork = (int64_t)M * nslot * 64;
+    if (i4 >= nwork) return;
+    const int m = (int)(i4 / (nslot * 64));
+    const int rem = (int)(i4 % (nslot * 64));
+    const int hs = rem / 64, d = rem % 64;
+    const int vc = 64 * (2 * hs + (d >> 5)) + (d & 31);
+    const float* pr = part + (int64_t)m * Nv;
+    float4 a = sum_split4(pr + vc, stride, splits);
+    float4 b = sum_split4(pr + vc + 32, stride, splits);
+    const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
+    float x1[4] = {a.x, a.y, a.z, a.w}, x2[4] = {b.x, b.y, b.z, b.w};
+    if (hs < e.Hq + e.Hkv) {
+      uint16_t* dst = (hs < e.Hq)
+          ? (uint16_t*)e.qo + (((int64_t)bs * e.Hq + hs) * e.R + ri) * 128
+          : (uint16_t*)e.kc + (((int64_t)bs * e.Hkv + (hs - e.Hq)) * e.Sp + pos) * 128;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float cs = e.rcos[(int64_t)pos * 64 + d + u], sn = e.rsin[(int64_t)pos * 64 + d + u];
+        dst[d + u] = f2bf(x1[u] * cs - x2[u] * sn);
+        dst[d + u + 64] = f2bf(x2[u] * cs + x1[u] * sn);
+      }
+    } else {
+      uint16_t* dst = (uint16_t*)e.vtc + ((int64_t)bs * e.Hkv + (hs - e.Hq - e.Hkv)) * 128 * (int64_t)e.Sp;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        dst[(int64_t)(d + u) * e.Sp + pos] = f2bf(x1[u]);
+        dst[(int64_t)(d + u + 64) * e.Sp + pos] = f2bf(x2[u]);
+      }
+    }
+  }
+}
+
+hipError_t launch_reduce_epilogue(int epi, const float* part, int splits, int M, int Nv,
+                                  const EpiArgs& e, hipStream_t st) {
+  int64_t n4 = 0;
+  if (epi == EPI_STORE || epi == EPI_F32) n4 = (int64_t)M * Nv / 4;
+  else if (epi == EPI_SWIGLU) n4 = (int64_t)M * e.F / 4;
+  else if (epi == EPI_QKV) n4 = (int64_t)M * (Nv / 128) * 16;
+  else return hipErrorInvalidValue;
+  if (n4 <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((n4 + 255) / 256);
+  switch (epi) {
+    case EPI_STORE: reduce_epilogue<EPI_STORE><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
+    case EPI_F32: reduce_epilogue<EPI_F32><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
+    case EPI_SWIGLU: reduce_epilogue<EPI_SWIGLU><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
+    case EPI_QKV: reduce_epilogue<EPI_QKV><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
+  }
+  return hipGetLastError();
+}
+
+// ============================================================================
 // planning and dispatch
 // ============================================================================
-GemmPlan gemm_plan(int dtype, int M, int Nv, int K) {
+GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   GemmPlan p;
-  p.ntn = (Nv + 127) / 128;
   if (dtype == F32) {
     p.kind = GEMM_F32;
+    p.ntn = (Nv + 127) / 128;
     p.ntm = (M + 31) / 32;
     p.kchunk = K;
     return p;
   }
-  int ks;
   if (M <= 64) {
     p.kind = GEMM_SKINNY;
-    p.mt = (M <= 32) ? 1 : 2;
+    p.mt = (M <= 16) ? 1 : (M <= 32) ? 2 : 4;
+    p.ntn = (Nv + S2_NT - 1) / S2_NT;
     p.ntm = 1;
-    ks = SK_KS;
-  } else {
-    p.kind = GEMM_TILED;
-    p.ntm = (M + 127) / 128;
-    ks = TB_K;
+    // K range per workgroup: the largest of 1024/512/256 dividing K whose activation
+    // slice fits the LDS budget (M > 32 rows: at most 512)
+    int kr = 256;
+    if (K % 1024 == 0 && p.mt <= 2) kr = 1024;
+    else if (K % 512 == 0) kr = 512;
+    p.kchunk = kr;
+    p.splits = K / kr;
+    p.part_floats = (size_t)p.splits * M * Nv + 64;  // + a trash slot for masked lanes
+    p.deferred = true;  // partials reduced by the next RMSNorm or by reduce_epilogue
+    return p;
   }
+  p.kind = GEMM_TILED;
+  p.ntn = (Nv + 127) / 128;
+  p.ntm = (M + 127) / 128;
+  const int ks = TB_K, target = 512;
   const int tiles = p.ntn * p.ntm;
-  const int target = 512;
   int splits = 1;
   if (tiles < target) {
     splits = (target + tiles - 1) / tiles;
@@ -419,9 +586,28 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K) {
   p.splits = (K + p.kchunk - 1) / p.kchunk;
   if (p.splits > 1) {
     p.part_floats = (size_t)p.splits * M * Nv;
-    p.counters = tiles;
+    p.deferred = (epi == EPI_RESID);
+    p.counters = p.deferred ? 0 : tiles;
   }
   return p;
+}
+
+hipError_t launch_gemm_only(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
+                            const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
+                            int* counters, hipStream_t st);
+
+static int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      n = cus;
+    else
+      n = 256;
+  }
+  return n;
 }
 
 template <int EPI>
@@ -432,15 +618,31 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
     gemm_f32<EPI><<<dim3(p.ntn, p.ntm), 256, 0, st>>>((const float*)X, ldx, (const float*)W, M,
                                                      Nv, K, e);
   } else if (p.kind == GEMM_SKINNY) {
-    dim3 grid(p.ntn, p.splits);
-    if (p.mt == 1)
-      gemm_skinny_bf16<EPI, 1><<<grid, 256, 0, st>>>((const uint16_t*)X, ldx, (const uint16_t*)W,
-                                                      M, Nv, K, p.kchunk, p.splits, part,
-                                                      counters, e);
-    else
-      gemm_skinny_bf16<EPI, 2><<<grid, 256, 0, st>>>((const uint16_t*)X, ldx, (const uint16_t*)W,
-                                                      M, Nv, K, p.kchunk, p.splits, part,
-                                                      counters, e);
+    // persistent: one 8-wave workgroup per CU, a whole number of workgroups per K range
+    int per_split = num_cus() / p.splits;
+    if (per_split < 1) per_split = 1;
+    if (per_split > p.ntn) per_split = p.ntn;
+    dim3 grid(per_split * p.splits);
+    const uint16_t* Xb = (const uint16_t*)X;
+    const uint16_t* Wb = (const uint16_t*)W;
+    constexpr int MAP = (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? EPI : EPI_STORE;
+    float* trash = part + (p.part_floats - 64);  // the trash slot past the partials
+#define DLLM_SKINNY(MTV, KRV)                                                           \
+    gemm_skinny_bf16<MAP, MTV, KRV><<<grid, 512, 0, st>>>(Xb, ldx, Wb, M, Nv, K, e.F,  \
+                                                         p.splits, p.ntn, part, trash)
+    if (p.mt == 1) {
+      if (p.kchunk == 1024) DLLM_SKINNY(1, 1024);
+      else if (p.kchunk == 512) DLLM_SKINNY(1, 512);
+      else DLLM_SKINNY(1, 256);
+    } else if (p.mt == 2) {
+      if (p.kchunk == 1024) DLLM_SKINNY(2, 1024);
+      else if (p.kchunk == 512) DLLM_SKINNY(2, 512);
+      else DLLM_SKINNY(2, 256);
+    } else {
+      if (p.kchunk == 512) DLLM_SKINNY(4, 512);
+      else DLLM_SKINNY(4, 256);
+    }
+#undef DLLM_SKINNY
   } else {
     gemm_tiled_bf16<EPI><<<dim3(p.ntn, p.ntm, p.splits), 256, 0, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, counters,
@@ -453,6 +655,16 @@ hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int
                        const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
                        int* counters, hipStream_t st) {
   if (M <= 0 || Nv <= 0) return hipSuccess;
+  hipError_t err = launch_gemm_only(dtype, epi, p, X, ldx, W, M, Nv, K, e, part, counters, st);
+  if (err != hipSuccess) return err;
+  if (p.kind == GEMM_SKINNY && epi != EPI_RESID)
+    return launch_reduce_epilogue(epi, part, p.splits, M, Nv, e, st);
+  return hipSuccess;
+}
+
+hipError_t launch_gemm_only(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
+                            const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
+                            int* counters, hipStream_t st) {
   switch (epi) {
     case EPI_STORE: return launch_epi<EPI_STORE>(dtype, p, X, ldx, W, M, Nv, K, e, part, counters, st);
     case EPI_F32: return launch_epi<EPI_F32>(dtype, p, X, ldx, W, M, Nv, K, e, part, counters, st);

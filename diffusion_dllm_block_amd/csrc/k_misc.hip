@@ -64,13 +64,83 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int* tokens, int 
   rms_row<T>(xr, g, eps, d, h + (int64_t)j * d, red);
 }
 
+// Single pass, the row held in registers: thread t owns columns 4t + 1024j (float4).
+// x = x + part[0] + ... + part[splits-1] (split order), written back; then
+// h = x / sqrt(mean(x^2) + eps) * g.  All loads of a thread are issued before the first
+// use.  Needs d % 1024 == 0 and d <= 8192 (the general kernel above covers the rest).
+template <typename T, int NJ>
+__global__ __launch_bounds__(256) void fold_norm_kernel(float* x, int Rin, int Kout, const T* g,
+                                                        float eps, int d, T* h,
+                                                        const float* part, int splits,
+                                                        int Mtot) {
+  __shared__ float red[4];
+  const int j0 = blockIdx.x;
+  const int64_t in_row = (int64_t)(j0 / Kout) * Rin + (j0 % Kout);
+  float* xr = x + in_row * d;
+  const int64_t stride = (int64_t)Mtot * d;
+  const float* pr = part + in_row * d;
+  float4 v[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) v[j] = *reinterpret_cast<const float4*>(xr + 4 * threadIdx.x + 1024 * j);
+  for (int s0 = 0; s0 < splits; s0 += 4) {
+    float4 pv[4][NJ];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        pv[u][j] = (s0 + u < splits)
+            ? *reinterpret_cast<const float4*>(pr + (s0 + u) * stride + 4 * threadIdx.x + 1024 * j)
+            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < splits)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          v[j].x += pv[u][j].x; v[j].y += pv[u][j].y; v[j].z += pv[u][j].z; v[j].w += pv[u][j].w;
+        }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    if (splits > 0) *reinterpret_cast<float4*>(xr + 4 * threadIdx.x + 1024 * j) = v[j];
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+  T* hr = h + (int64_t)j0 * d;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int c = 4 * threadIdx.x + 1024 * j;
+    Elt<T>::store(hr, c + 0, (v[j].x * r) * Elt<T>::load(g, c + 0));
+    Elt<T>::store(hr, c + 1, (v[j].y * r) * Elt<T>::load(g, c + 1));
+    Elt<T>::store(hr, c + 2, (v[j].z * r) * Elt<T>::load(g, c + 2));
+    Elt<T>::store(hr, c + 3, (v[j].w * r) * Elt<T>::load(g, c + 3));
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* x, int Rin, int Kout,
-                                                      const T* g, float eps, int d, T* h) {
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, int Rin, int Kout, const T* g,
+                                                      float eps, int d, T* h, const float* part,
+                                                      int splits, int Mtot) {
   __shared__ float red[4];
   int j = blockIdx.x;
   int64_t in_row = (int64_t)(j / Kout) * Rin + (j % Kout);
-  rms_row<T>(x + in_row * d, g, eps, d, h + (int64_t)j * d, red);
+  float* xr = x + in_row * d;
+  if (splits > 0) {
+    // add the pending split-K partials of the residual GEMM, in split order
+    const float* pr = part + in_row * d;
+    const int64_t stride = (int64_t)Mtot * d;
+    for (int c = threadIdx.x; c < d; c += blockDim.x) {
+      float v = xr[c];
+      for (int s = 0; s < splits; ++s) v += pr[s * stride + c];
+      xr[c] = v;
+    }
+    __syncthreads();
+  }
+  rms_row<T>(xr, g, eps, d, h + (int64_t)j * d, red);
 }
 
 hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R, int B,
@@ -87,14 +157,51 @@ hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R,
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(int dtype, const float* x, int rows, int Rin, int Kout, const void* g,
-                          float eps, int d, void* h, hipStream_t st) {
+hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
+                          float eps, int d, void* h, const float* part, int splits, int Mtot,
+                          hipStream_t st) {
   if (rows <= 0) return hipSuccess;
+  if (d % 1024 == 0 && d <= 8192) {
+    const int nj = d / 1024;
+#define DLLM_FOLD(TT, NJV)                                                                  \
+  fold_norm_kernel<TT, NJV><<<rows, 256, 0, st>>>(x, Rin, Kout, (const TT*)g, eps, d, (TT*)h, \
+                                                  part, splits, Mtot)
+    if (dtype == F32) {
+      switch (nj) { case 1: DLLM_FOLD(float, 1); break; case 2: DLLM_FOLD(float, 2); break;
+                    case 4: DLLM_FOLD(float, 4); break; default: goto general; }
+    } else {
+      switch (nj) { case 1: DLLM_FOLD(uint16_t, 1); break; case 2: DLLM_FOLD(uint16_t, 2); break;
+                    case 4: DLLM_FOLD(uint16_t, 4); break; case 8: DLLM_FOLD(uint16_t, 8); break;
+                    default: goto general; }
+    }
+#undef DLLM_FOLD
+    return hipGetLastError();
+  }
+general:
   if (dtype == F32)
-    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, Rin, Kout, (const float*)g, eps, d, (float*)h);
+    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, Rin, Kout, (const float*)g, eps, d, (float*)h,
+                                                part, splits, Mtot);
   else
     rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(x, Rin, Kout, (const uint16_t*)g, eps, d,
-                                                   (uint16_t*)h);
+                                                   (uint16_t*)h, part, splits, Mtot);
+  return hipGetLastError();
+}
+
+__global__ void fold_partials_kernel(float* y, const float* part, int splits, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    float v = y[i];
+    for (int s = 0; s < splits; ++s) v += part[s * n + i];
+    y[i] = v;
+  }
+}
+
+hipError_t launch_fold_partials(float* y, const float* part, int splits, int64_t n,
+                                hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  fold_partials_kernel<<<blocks, 256, 0, st>>>(y, part, splits, n);
   return hipGetLastError();
 }
 

@@ -42,9 +42,10 @@ struct GemmPlan {
   int splits = 1, kchunk = 0;
   size_t part_floats = 0;  // split-K partial buffer
   int counters = 0;        // split-K arrival counters
+  bool deferred = false;   // residual partials left for the next RMSNorm to add
 };
 
-GemmPlan gemm_plan(int dtype, int M, int Nv, int K);
+GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi);
 hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
                        const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
                        int* counters, hipStream_t st);
@@ -52,9 +53,9 @@ hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int
 // ---------------------------------------------------------------- attention
 struct AttnPlan {
   int kind = 0;          // 0: fp32 simple, 1: bf16 split-KV (R <= 64), 2: bf16 flash
-  int nqt = 0, nchunk = 0;
+  int nqt = 0, nchunk = 0, nsub = 0;
   size_t part_floats = 0;
-  int counters = 0;
+  int counters = 0;      // unused: chunk partials are merged by a second kernel
 };
 AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D);
 hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const void* k,
@@ -80,9 +81,15 @@ hipError_t launch_rope_table(float* cosb, float* sinb, int S, int D, float theta
 hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R, int B,
                              const void* embed, const void* g, float eps, int d, int V, float* x,
                              void* h, hipStream_t st);
-// h[j] = rmsnorm(x[in_row(j)]) * g, in_row(j) = (j / Kout) * Rin + j % Kout, j < rows
-hipError_t launch_rmsnorm(int dtype, const float* x, int rows, int Rin, int Kout,
-                          const void* g, float eps, int d, void* h, hipStream_t st);
+// h[j] = rmsnorm(x[in_row(j)]) * g, in_row(j) = (j / Kout) * Rin + j % Kout, j < rows.
+// With splits > 0, first x[in_row] += part[0][in_row] + ... + part[splits-1][in_row]
+// (part is [splits][Mtot][d] fp32, written back into x).
+hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
+                          float eps, int d, void* h, const float* part, int splits, int Mtot,
+                          hipStream_t st);
+// y[i] += part[0][i] + ... + part[splits-1][i], i < n  (n = M * N)
+hipError_t launch_fold_partials(float* y, const float* part, int splits, int64_t n,
+                                hipStream_t st);
 hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st);
 hipError_t launch_synth_fill(void* dst, int64_t n, int dtype, uint64_t seed, uint32_t tid,
                              double stdv, int mode, hipStream_t st);

@@ -85,8 +85,12 @@ dllm_status check_model(const dllm_model_desc* m) {
     return fail(DLLM_E_UNSUPPORTED, "head_dim must be even and divide 128");
   if (m->d_model % 64 || m->d_ffn % 64 || (m->n_heads * m->head_dim) % 64)
     return fail(DLLM_E_UNSUPPORTED, "d_model, d_ffn and n_heads*head_dim must be multiples of 64");
-  if (m->dtype == DLLM_BF16 && (m->head_dim != 128 || m->d_model % 128 || m->d_ffn % 128))
-    return fail(DLLM_E_UNSUPPORTED, "bf16 models need head_dim 128 and d_model, d_ffn multiples of 128");
+  if (m->dtype == DLLM_BF16 &&
+      (m->head_dim != 128 || m->d_model % 256 || m->d_ffn % 256 || (m->n_heads * 128) % 256 ||
+       m->vocab % 8))
+    return fail(DLLM_E_UNSUPPORTED,
+                "bf16 models need head_dim 128, d_model, d_ffn, n_heads*128 multiples of 256 "
+                "and vocab a multiple of 8");
   if (m->mask_id < 0 || m->mask_id >= m->vocab) return fail(DLLM_E_ARG, "mask_id outside [0, vocab)");
   if (!std::isfinite(m->rope_theta) || m->rope_theta <= 0.f) return fail(DLLM_E_ARG, "bad rope_theta");
   if (!std::isfinite(m->norm_eps) || m->norm_eps < 0.f) return fail(DLLM_E_ARG, "bad norm_eps");
@@ -141,9 +145,11 @@ struct Ws {
 
 void plan_gemms(const Dims& d, int M, bool lm, size_t* pf, int* cn) {
   const int Nqkv = (d.Hq + 2 * d.Hkv) * d.D;
-  GemmPlan ps[5] = {gemm_plan(d.dtype, M, Nqkv, d.d), gemm_plan(d.dtype, M, d.d, d.Hq * d.D),
-                    gemm_plan(d.dtype, M, 2 * d.F, d.d), gemm_plan(d.dtype, M, d.d, d.F),
-                    gemm_plan(d.dtype, d.B * d.K, d.V, d.d)};
+  GemmPlan ps[5] = {gemm_plan(d.dtype, M, Nqkv, d.d, EPI_QKV),
+                    gemm_plan(d.dtype, M, d.d, d.Hq * d.D, EPI_RESID),
+                    gemm_plan(d.dtype, M, 2 * d.F, d.d, EPI_SWIGLU),
+                    gemm_plan(d.dtype, M, d.d, d.F, EPI_RESID),
+                    gemm_plan(d.dtype, d.B * d.K, d.V, d.d, EPI_F32)};
   for (int i = 0; i < (lm ? 5 : 4); ++i) {
     if (ps[i].part_floats > *pf) *pf = ps[i].part_floats;
     if (ps[i].counters > *cn) *cn = ps[i].counters;
@@ -214,6 +220,11 @@ dllm_status check_buffers(const Dims& d, const dllm_seq_desc* s, Ws* w) {
 }
 
 // ------------------------------------------------------------------ execution
+struct Pending {  // split-K partials of a residual GEMM not yet added into x
+  int splits = 0;
+  int M = 0;
+};
+
 struct Ctx {
   const Dims& d;
   const dllm_model_desc* m;
@@ -221,6 +232,7 @@ struct Ctx {
   Ws w;
   char* ws;
   hipStream_t st;
+  mutable Pending pend;
   template <typename P> P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
   void* cache_k(int l) const {
     return (char*)s->kv_cache + (size_t)l * 2 * d.B * d.Hkv * d.Sp * d.D * d.esz;
@@ -232,12 +244,28 @@ struct Ctx {
 
 dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const void* W, int M,
                  int Nv, int K, const EpiArgs& e) {
-  GemmPlan p = gemm_plan(c.d.dtype, M, Nv, K);
+  GemmPlan p = gemm_plan(c.d.dtype, M, Nv, K, epi);
   if (p.part_floats > c.w.gpart_floats || p.counters > c.w.gcnt_n)
     return fail(DLLM_E_WORKSPACE, "internal: GEMM plan exceeds the workspace plan");
+  if (c.pend.splits)
+    return fail(DLLM_E_STATE, "internal: pending residual partials not consumed");
   ProfScope ps(cls, c.st);
   HIP_TRY(launch_gemm(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, e, c.at<float>(c.w.gpart),
                       c.at<int>(c.w.gcnt), c.st));
+  if (p.deferred && epi == EPI_RESID) {
+    c.pend.splits = p.splits;
+    c.pend.M = M;
+  }
+  return DLLM_OK;
+}
+
+// RMSNorm of `rows` rows of x into h (see launch_rmsnorm); adds pending residual partials.
+dllm_status norm(const Ctx& c, int rows, int Rin, int Kout, const void* g) {
+  ProfScope ps(DLLM_K_RMSNORM, c.st);
+  HIP_TRY(launch_rmsnorm(c.d.dtype, c.at<float>(c.w.x), rows, Rin, Kout, g, c.d.eps, c.d.d,
+                         c.at<void>(c.w.h), c.at<float>(c.w.gpart), c.pend.splits, c.pend.M,
+                         c.st));
+  c.pend = Pending{};
   return DLLM_OK;
 }
 
@@ -261,8 +289,8 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
   const int Nqkv = (d.Hq + 2 * d.Hkv) * d.D;
   for (int l = 0; l < d.L; ++l) {
     if (l > 0) {
-      ProfScope ps(DLLM_K_RMSNORM, c.st);
-      HIP_TRY(launch_rmsnorm(d.dtype, x, M, R, R, c.m->attn_norm[l], d.eps, d.d, h, c.st));
+      dllm_status st = norm(c, M, R, R, c.m->attn_norm[l]);
+      if (st) return st;
     }
     EpiArgs eq;
     eq.qo = q; eq.kc = c.cache_k(l); eq.vtc = c.cache_vt(l);
@@ -283,10 +311,8 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
     st = gemm(c, refresh ? DLLM_K_REF_O : DLLM_K_STEP_O, EPI_RESID, o, d.Hq * d.D, c.m->w_o[l], M,
               d.d, d.Hq * d.D, er);
     if (st) return st;
-    {
-      ProfScope ps(DLLM_K_RMSNORM, c.st);
-      HIP_TRY(launch_rmsnorm(d.dtype, x, M, R, R, c.m->ffn_norm[l], d.eps, d.d, h, c.st));
-    }
+    st = norm(c, M, R, R, c.m->ffn_norm[l]);
+    if (st) return st;
     EpiArgs eg;
     eg.y = a; eg.F = d.F;
     st = gemm(c, refresh ? DLLM_K_REF_GATE_UP : DLLM_K_STEP_GATE_UP, EPI_SWIGLU, h, d.d,
@@ -299,7 +325,11 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
   return DLLM_OK;
 }
 
-dllm_status do_refresh(const Ctx& c) { return run_layers(c, 0, c.d.S, true); }
+dllm_status do_refresh(const Ctx& c) {
+  dllm_status st = run_layers(c, 0, c.d.S, true);
+  c.pend = Pending{};  // the last layer's tail is skipped: nothing is pending
+  return st;
+}
 
 dllm_status do_init(const Ctx& c) {
   const Dims& d = c.d;
@@ -317,11 +347,8 @@ dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, flo
   dllm_status st = run_layers(c, s0, R, false);
   if (st) return st;
   void* h = c.at<void>(c.w.h);
-  {
-    ProfScope ps(DLLM_K_RMSNORM, c.st);
-    HIP_TRY(launch_rmsnorm(d.dtype, c.at<float>(c.w.x), d.B * d.K, R, d.K, c.m->final_norm,
-                           d.eps, d.d, h, c.st));
-  }
+  st = norm(c, d.B * d.K, R, d.K, c.m->final_norm);
+  if (st) return st;
   float* lg = logits ? logits : c.at<float>(c.w.logits);
   EpiArgs el;
   el.y = lg; el.ldy = d.V; el.scale = d.lscale;
@@ -538,9 +565,15 @@ dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dty
 
 size_t dllm_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype) {
   if (M < 1 || N < 1 || K < 1) return 0;
-  GemmPlan p = gemm_plan(dtype, M, N, K);
-  return up((size_t)p.counters * 4) + up(p.part_floats * 4) + kAlign;
+  size_t best = 0;
+  for (int epi : {EPI_STORE, EPI_F32, EPI_RESID}) {
+    GemmPlan p = gemm_plan(dtype, M, N, K, epi);
+    size_t b = up((size_t)p.counters * 4) + up(p.part_floats * 4) + kAlign;
+    if (b > best) best = b;
+  }
+  return best;
 }
+
 
 dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
                                int32_t K, int32_t dtype, int32_t mode, float scale, void* ws,
@@ -549,9 +582,11 @@ dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M,
   if (dtype != DLLM_F32 && dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype");
   if (mode < 0 || mode > 2) return fail(DLLM_E_ARG, "bad mode");
   if (M < 1 || N < 1 || K < 1) return fail(DLLM_E_SHAPE, "sizes must be positive");
-  if (dtype == DLLM_BF16 && K % 128) return fail(DLLM_E_UNSUPPORTED, "bf16 needs K %% 128 == 0");
+  if (dtype == DLLM_BF16 && (K % 256 || N % 8))
+    return fail(DLLM_E_UNSUPPORTED, "bf16 needs K %% 256 == 0 and N %% 8 == 0");
   if (dtype == DLLM_F32 && K % 16) return fail(DLLM_E_UNSUPPORTED, "fp32 needs K %% 16 == 0");
-  GemmPlan p = gemm_plan(dtype, M, N, K);
+  int epi = mode == 0 ? EPI_STORE : mode == 1 ? EPI_F32 : EPI_RESID;
+  GemmPlan p = gemm_plan(dtype, M, N, K, epi);
   size_t need = up((size_t)p.counters * 4) + up(p.part_floats * 4);
   if (need && (!ws || ws_bytes < need)) return fail(DLLM_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
@@ -560,8 +595,9 @@ dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M,
   if (p.counters) HIP_TRY(launch_fill_i32(cnt, p.counters, 0, st));
   EpiArgs e;
   e.y = y; e.ldy = N; e.scale = scale;
-  int epi = mode == 0 ? EPI_STORE : mode == 1 ? EPI_F32 : EPI_RESID;
   HIP_TRY(launch_gemm(dtype, epi, p, x, K, w, M, N, K, e, part, cnt, st));
+  if (p.deferred && epi == EPI_RESID)
+    HIP_TRY(launch_fold_partials((float*)y, part, p.splits, (int64_t)M * N, st));
   return DLLM_OK;
 }
 

@@ -79,7 +79,10 @@ typedef enum { DLLM_CACHE_PREFIX = 1, DLLM_CACHE_DUAL = 2 } dllm_cache_mode;
 /* Model weights.  Shapes are row-major; "T" is float (DLLM_F32) or bf16 (DLLM_BF16).
  * Supported: head_dim divides 128 (and is even); n_heads % n_kv_heads == 0;
  * d_model, d_ffn and n_heads*head_dim multiples of 64; for DLLM_BF16 also head_dim ==
- * 128 and d_model, d_ffn multiples of 128.  mask_id in [0, vocab).                   */
+ * 128, d_model, d_ffn, n_heads*head_dim multiples of 256 and vocab a multiple of 8.
+ * mask_id in [0, vocab).
+ * Token ids in `tokens` must lie in [0, vocab) (others are clamped, never read out of
+ * bounds).                                                                           */
 typedef struct {
   int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, mask_id;
   float rope_theta, norm_eps, logit_scale;
@@ -202,7 +205,8 @@ dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dty
 
 /* y = x W^T for x T [M][K], W T [N][K].  mode 0: y T [M][N]; mode 1: y fp32 [M][N] =
  * scale * x W^T; mode 2: y fp32 [M][N] += x W^T (residual add).  Same kernels as the
- * model path (MFMA for DLLM_BF16: K % 128 == 0).  ws from dllm_linear_workspace_bytes. */
+ * model path (MFMA for DLLM_BF16: K % 256 == 0, N % 8 == 0; fp32: K % 16 == 0).  ws from
+ * dllm_linear_workspace_bytes().                                                     */
 size_t dllm_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t dtype);
 dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M, int32_t N,
                                int32_t K, int32_t dtype, int32_t mode, float scale, void* ws,

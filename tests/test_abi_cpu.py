@@ -138,5 +138,6 @@ def test_kernel_entry_validation(lib):
              0, None) == -4
     h = lib.cdll.dllm_kernel_linear
     assert h(FAKE, FAKE, FAKE, 4, 4, 100, bd.BF16, 0, 1.0, None, 0, None) == -3
-    assert h(FAKE, FAKE, FAKE, 4, 4, 128, bd.BF16, 3, 1.0, None, 0, None) == -7
+    assert h(FAKE, FAKE, FAKE, 4, 4, 256, bd.BF16, 3, 1.0, None, 0, None) == -7
+    assert h(FAKE, FAKE, FAKE, 4, 4, 384, bd.BF16, 0, 1.0, None, 0, None) == -3
     assert lib.cdll.dllm_profile_select(99) == -7
