@@ -37,7 +37,7 @@ PEAK_F32_VALU_TFLOPS = 157.3
 # Dominant kernel class per workload (largest summed duration in the rocprofv3 kernel
 # trace of this benchmark; see profiles/).
 DOMINANT = {
-    "llada8b_dual_p1000_g1024": "REF_GATE_UP",
+    "llada8b_dual_p1000_g1024": "STEP_GATE_UP",
     "llada8b_prefix_p256_g256": "STEP_GATE_UP",
     "dream7b_dual_b8_p512_g512": "REF_GATE_UP",
     "tiny_dual": "STEP_GATE_UP",

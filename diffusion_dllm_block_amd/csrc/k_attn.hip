@@ -441,7 +441,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
     p.kind = 1;
     p.nqt = (R + 31) / 32;
     const int base = B * Hq * p.nqt;
-    int target = (512 + base - 1) / base;          // chunks wanted for ~512 workgroups
+    int target = (256 + base - 1) / base;          // chunks wanted for ~256 workgroups
     if (target < 1) target = 1;
     int ck = (S + target - 1) / target;             // keys per chunk
     ck = (ck + 127) / 128 * 128;                    // 4 waves x 32-key sub-tiles

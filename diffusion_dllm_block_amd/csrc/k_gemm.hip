@@ -154,50 +154,42 @@ __device__ __forceinline__ int wrow_s2(int vc, int F) {
   }
 }
 
-// Tiles of 64 virtual columns.  Workgroup = 8 waves: wave w owns columns 16*(w&3)..+16 and
-// the (w>>2)-th half of the workgroup's K range (KR).  XV = 16-byte activation loads per
-// thread to fill the LDS slice; NLOAD = weight loads per lane per tile.
+// Workgroup = 8 independent waves pinned to one K range of KR.  Each wave computes 16
+// virtual columns over the whole K range (NLOAD = KR/32 weight loads of 16 bytes per lane
+// in flight).  XV = 16-byte activation loads per thread to fill the LDS slice.
 template <int MT, int KR> struct SkinnyCfg {
-  static constexpr int KW = KR / 2;
-  static constexpr int NLOAD = KW / 32;
+  static constexpr int NLOAD = KR / 32;
   static constexpr int LDX = KR + 8;                 // LDS row stride (elements)
   static constexpr int XV = MT * 16 * KR / 8 / 512;
   static_assert(XV >= 1, "activation slice smaller than one load per thread");
 };
 
 // Persistent weight-streaming GEMM for M <= 64 rows.
-//   * The grid holds one workgroup per CU; a workgroup is pinned to one K range
-//     (blockIdx % splits) and walks the column tiles tn = wid, wid + nw, ...
-//   * Its activation slice X[M][KR] is loaded into LDS once.
+//   * One workgroup per CU, pinned to one K range (blockIdx % splits); its activation
+//     slice X[M][KR] is loaded into LDS once.
+//   * Its 8 waves walk 16-column groups independently (group = wid*8 + wave, then + nw*8):
+//     no barrier after the slice is loaded.
 //   * Each lane keeps NLOAD weight loads in flight: register t is refilled with the next
-//     tile's weights right after the MFMAs of step t consumed it, so the weight stream
-//     does not pause between tiles.  After the last tile the refills read a fixed cached
-//     line instead of branching, and every tile writes its split partials through
-//     unconditional stores (out-of-range lanes write a trash slot): the loop has no
-//     data-dependent branches, which keeps the compiler's wait counts exact.
-//   * Partials [split][M][Nv] (virtual column order) are summed in split order by
+//     group's weights right after the MFMAs of step t consumed it, so the weight stream
+//     does not pause between groups.  After the last group the refills read one fixed
+//     cached line instead of branching, and every group writes its whole padded block
+//     of partials: no data-dependent branches, so the compiler's wait counts stay exact.
+//   * Partials (blocked layout, virtual column order) are summed in split order by
 //     reduce_epilogue, or for the residual GEMMs by the next RMSNorm.
 template <int MAP, int MT, int KR>
-__global__ __launch_bounds__(512, 1) void gemm_skinny_bf16(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_skinny_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv,
-    int K, int F, int splits, int ntn, float* __restrict__ part, float* __restrict__ trash) {
+    int K, int F, int splits, int ngrp, float* __restrict__ part) {
   using C = SkinnyCfg<MT, KR>;
   __shared__ __attribute__((aligned(16))) uint16_t Xs[MT * 16 * C::LDX];
-  __shared__ float red[MT * 16 * S2_TL];
   const int split = blockIdx.x % splits;
   const int wid = blockIdx.x / splits;
   const int nw = gridDim.x / splits;  // workgroups per K range (grid is a multiple of splits)
-  if (wid >= ntn) return;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, ng = w & 3, kg = w >> 2, l = tid & 63, ln = l & 15, g = l >> 4;
+  const int w = tid >> 6, l = tid & 63, ln = l & 15, g = l >> 4;
   const int kb = split * KR;
 
-  auto wptr = [&](int tn) {  // columns past Nv read a clamped valid row (never stored)
-    const int vc = min(tn * S2_NT + ng * 16 + ln, Nv - 1);
-    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + kb + kg * C::KW + 8 * g;
-  };
-
-  {  // activation slice -> LDS (rows >= M read row M-1; never stored)
+  {  // activation slice -> LDS (rows >= M read row M-1; their outputs are never used)
     u32x4 xr[C::XV];
 #pragma unroll
     for (int i = 0; i < C::XV; ++i) {
@@ -212,59 +204,58 @@ __global__ __launch_bounds__(512, 1) void gemm_skinny_bf16(
       *reinterpret_cast<u32x4*>(&Xs[r * C::LDX + 8 * c8]) = xr[i];
     }
   }
+  __syncthreads();
+  const int grp0 = wid * 8 + w;
+  if (grp0 >= ngrp) return;  // no barrier follows
+
+  auto wptr = [&](int grp) {  // columns past Nv read a clamped valid row (never used)
+    const int vc = min(grp * 16 + ln, Nv - 1);
+    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + kb + 8 * g;
+  };
   u32x4 wr[C::NLOAD];
   {
-    const uint16_t* wp = wptr(wid);
+    const uint16_t* wp = wptr(grp0);
 #pragma unroll
     for (int t = 0; t < C::NLOAD; ++t)
-      wr[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wp + 32 * t));
+      wr[t] = *reinterpret_cast<const u32x4*>(wp + 32 * t);
   }
-  __syncthreads();
 
-  for (int tn = wid; tn < ntn; tn += nw) {
-    const bool has_next = tn + nw < ntn;
-    // refill source: the next tile, or (after the last tile) one fixed line, step 0
-    const uint16_t* wpn = has_next ? wptr(tn + nw) : W;
-    const int tstride = has_next ? 32 : 0;
+  for (int grp = grp0; grp < ngrp; grp += nw * 8) {
+    const bool has_next = grp + nw * 8 < ngrp;
+    // refill source: the next group, or (after the last group) the first KR elements of
+    // W, which stay cached; the same offsets keep the loads' addresses immediate
+    const uint16_t* wpn = has_next ? wptr(grp + nw * 8) : W + 8 * g;
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
+    // activation operands are read one step ahead; the scheduling barrier keeps the
+    // compiler from hoisting every LDS read (which would need ~2*NLOAD*MT registers)
+    const uint16_t* xs = &Xs[ln * C::LDX + 8 * g];
+    u32x4 a_cur[MT], a_nxt[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      a_cur[mt] = *reinterpret_cast<const u32x4*>(xs + mt * 16 * C::LDX);
 #pragma unroll
     for (int t = 0; t < C::NLOAD; ++t) {
+      if (t + 1 < C::NLOAD) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        u32x4 a = *reinterpret_cast<const u32x4*>(
-            &Xs[(mt * 16 + ln) * C::LDX + kg * C::KW + 32 * t + 8 * g]);
-        acc[mt] = mfma16(as_bf16x8(a), as_bf16x8(wr[t]), acc[mt]);
+        for (int mt = 0; mt < MT; ++mt)
+          a_nxt[mt] = *reinterpret_cast<const u32x4*>(xs + mt * 16 * C::LDX + 32 * (t + 1));
       }
-      wr[t] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wpn + tstride * t));
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(as_bf16x8(a_cur[mt]), as_bf16x8(wr[t]), acc[mt]);
+      wr[t] = *reinterpret_cast<const u32x4*>(wpn + 32 * t);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) a_cur[mt] = a_nxt[mt];
+      __builtin_amdgcn_sched_barrier(0);
     }
-
-    // sum the two K halves: red[m][c], c = 16*ng + column-in-MFMA
-    if (kg == 1) {
+    // lane (column ln, group g) holds rows mt*16 + 4g + r: blocked partial layout, one
+    // 256-byte contiguous store per (mt, r) (PartView in kernels.h)
+    float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[(mt * 16 + 4 * g + r) * S2_TL + ng * 16 + ln] = acc[mt][r];
-    }
-    __syncthreads();
-    if (kg == 0) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) red[(mt * 16 + 4 * g + r) * S2_TL + ng * 16 + ln] += acc[mt][r];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < MT * 16 * S2_NT / 512; ++i) {
-      const int idx = tid + 512 * i;
-      const int r = idx >> 6, c = idx & 63;
-      const int vcc = tn * S2_NT + c;
-      const bool ok = (r < M) && (vcc < Nv);
-      float* dst = ok ? part + ((int64_t)split * M + r) * Nv + vcc : trash + l;
-      *dst = red[r * S2_TL + c];
-    }
-    __syncthreads();  // red is reused by the next tile
+      for (int r = 0; r < 4; ++r) blk[(mt * 4 + r) * 64 + l] = acc[mt][r];
   }
 }
 
@@ -443,31 +434,32 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int
 // split-K reduction + epilogue for the skinny GEMM (partials in 64-column virtual order)
 // ============================================================================
 // One thread per 4 consecutive outputs; partials summed in split order.
-__device__ __forceinline__ float4 sum_split4(const float* p, int64_t stride, int splits) {
+__device__ __forceinline__ float4 sum_split4(const PartView& pv, int m, int c) {
+  const int64_t stride = pv.split_stride();
+  const float* p = pv.p + pv.off(m, c);
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < splits; s0 += 4) {
+  for (int s0 = 0; s0 < pv.splits; s0 += 4) {
     float4 v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      v[u] = (s0 + u < splits) ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = (s0 + u < pv.splits) ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (s0 + u < splits) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+      if (s0 + u < pv.splits) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
   }
   return s;
 }
 
 template <int EPI>
-__global__ __launch_bounds__(256) void reduce_epilogue(const float* __restrict__ part, int splits,
-                                                       int M, int Nv, EpiArgs e) {
-  const int64_t stride = (int64_t)M * Nv;
+__global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
+  const int M = pv.M, Nv = pv.N;
   const int64_t i4 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
   if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
     // Nv % 4 == 0: 4 outputs of one row
-    if (i4 >= stride) return;
+    if (i4 >= (int64_t)M * Nv) return;
     const int m = (int)(i4 / Nv), vc = (int)(i4 % Nv);
-    float4 v = sum_split4(part + i4, stride, splits);
+    float4 v = sum_split4(pv, m, vc);
     if constexpr (EPI == EPI_F32) {
       float4 o = make_float4(v.x * e.scale, v.y * e.scale, v.z * e.scale, v.w * e.scale);
       *reinterpret_cast<float4*>((float*)e.y + (int64_t)m * e.ldy + vc) = o;
@@ -477,28 +469,24 @@ __global__ __launch_bounds__(256) void reduce_epilogue(const float* __restrict__
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // output column c of row m: gate at virtual column 64(c/32) + c%32, up 32 further
-    const int64_t nout = (int64_t)M * e.F;
-    if (i4 >= nout) return;
+    if (i4 >= (int64_t)M * e.F) return;
     const int m = (int)(i4 / e.F), c = (int)(i4 % e.F);
     const int vg = 64 * (c >> 5) + (c & 31);
-    const float* pr = part + (int64_t)m * Nv;
-    float4 gt = sum_split4(pr + vg, stride, splits);
-    float4 up = sum_split4(pr + vg + 32, stride, splits);
+    float4 gt = sum_split4(pv, m, vg);
+    float4 up = sum_split4(pv, m, vg + 32);
     uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.F + c;
     y[0] = f2bf(silu(gt.x) * up.x); y[1] = f2bf(silu(gt.y) * up.y);
     y[2] = f2bf(silu(gt.z) * up.z); y[3] = f2bf(silu(gt.w) * up.w);
   } else if constexpr (EPI == EPI_QKV) {
     // (row m, head slot hs, dims d..d+3 < 64) -> pairs (d, d+64); head_dim 128
     const int nslot = Nv / 128;
-    const int64_t nwork = (int64_t)M * nslot * 64;
-    if (i4 >= nwork) return;
+    if (i4 >= (int64_t)M * nslot * 64) return;
     const int m = (int)(i4 / (nslot * 64));
     const int rem = (int)(i4 % (nslot * 64));
     const int hs = rem / 64, d = rem % 64;
     const int vc = 64 * (2 * hs + (d >> 5)) + (d & 31);
-    const float* pr = part + (int64_t)m * Nv;
-    float4 a = sum_split4(pr + vc, stride, splits);
-    float4 b = sum_split4(pr + vc + 32, stride, splits);
+    float4 a = sum_split4(pv, m, vc);
+    float4 b = sum_split4(pv, m, vc + 32);
     const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
     float x1[4] = {a.x, a.y, a.z, a.w}, x2[4] = {b.x, b.y, b.z, b.w};
     if (hs < e.Hq + e.Hkv) {
@@ -522,20 +510,19 @@ __global__ __launch_bounds__(256) void reduce_epilogue(const float* __restrict__
   }
 }
 
-hipError_t launch_reduce_epilogue(int epi, const float* part, int splits, int M, int Nv,
-                                  const EpiArgs& e, hipStream_t st) {
+hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e, hipStream_t st) {
   int64_t n4 = 0;
-  if (epi == EPI_STORE || epi == EPI_F32) n4 = (int64_t)M * Nv / 4;
-  else if (epi == EPI_SWIGLU) n4 = (int64_t)M * e.F / 4;
-  else if (epi == EPI_QKV) n4 = (int64_t)M * (Nv / 128) * 16;
+  if (epi == EPI_STORE || epi == EPI_F32) n4 = (int64_t)pv.M * pv.N / 4;
+  else if (epi == EPI_SWIGLU) n4 = (int64_t)pv.M * e.F / 4;
+  else if (epi == EPI_QKV) n4 = (int64_t)pv.M * (pv.N / 128) * 16;
   else return hipErrorInvalidValue;
   if (n4 <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n4 + 255) / 256);
   switch (epi) {
-    case EPI_STORE: reduce_epilogue<EPI_STORE><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
-    case EPI_F32: reduce_epilogue<EPI_F32><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
-    case EPI_SWIGLU: reduce_epilogue<EPI_SWIGLU><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
-    case EPI_QKV: reduce_epilogue<EPI_QKV><<<blocks, 256, 0, st>>>(part, splits, M, Nv, e); break;
+    case EPI_STORE: reduce_epilogue<EPI_STORE><<<blocks, 256, 0, st>>>(pv, e); break;
+    case EPI_F32: reduce_epilogue<EPI_F32><<<blocks, 256, 0, st>>>(pv, e); break;
+    case EPI_SWIGLU: reduce_epilogue<EPI_SWIGLU><<<blocks, 256, 0, st>>>(pv, e); break;
+    case EPI_QKV: reduce_epilogue<EPI_QKV><<<blocks, 256, 0, st>>>(pv, e); break;
   }
   return hipGetLastError();
 }
@@ -564,7 +551,7 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     else if (K % 512 == 0) kr = 512;
     p.kchunk = kr;
     p.splits = K / kr;
-    p.part_floats = (size_t)p.splits * M * Nv + 64;  // + a trash slot for masked lanes
+    p.part_floats = (size_t)p.splits * ((Nv + 15) / 16) * (p.mt * 16 * 16);  // blocked layout
     p.deferred = true;  // partials reduced by the next RMSNorm or by reduce_epilogue
     return p;
   }
@@ -619,17 +606,17 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
                                                      Nv, K, e);
   } else if (p.kind == GEMM_SKINNY) {
     // persistent: one 8-wave workgroup per CU, a whole number of workgroups per K range
+    const int ngrp = (Nv + 15) / 16;
     int per_split = num_cus() / p.splits;
     if (per_split < 1) per_split = 1;
-    if (per_split > p.ntn) per_split = p.ntn;
+    if (per_split > (ngrp + 7) / 8) per_split = (ngrp + 7) / 8;
     dim3 grid(per_split * p.splits);
     const uint16_t* Xb = (const uint16_t*)X;
     const uint16_t* Wb = (const uint16_t*)W;
     constexpr int MAP = (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? EPI : EPI_STORE;
-    float* trash = part + (p.part_floats - 64);  // the trash slot past the partials
 #define DLLM_SKINNY(MTV, KRV)                                                           \
     gemm_skinny_bf16<MAP, MTV, KRV><<<grid, 512, 0, st>>>(Xb, ldx, Wb, M, Nv, K, e.F,  \
-                                                         p.splits, p.ntn, part, trash)
+                                                         p.splits, ngrp, part)
     if (p.mt == 1) {
       if (p.kchunk == 1024) DLLM_SKINNY(1, 1024);
       else if (p.kchunk == 512) DLLM_SKINNY(1, 512);
@@ -658,7 +645,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int
   hipError_t err = launch_gemm_only(dtype, epi, p, X, ldx, W, M, Nv, K, e, part, counters, st);
   if (err != hipSuccess) return err;
   if (p.kind == GEMM_SKINNY && epi != EPI_RESID)
-    return launch_reduce_epilogue(epi, part, p.splits, M, Nv, e, st);
+    return launch_reduce_epilogue(epi, p.view(part, M, Nv), e, st);
   return hipSuccess;
 }
 

@@ -70,40 +70,38 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int* tokens, int 
 // use.  Needs d % 1024 == 0 and d <= 8192 (the general kernel above covers the rest).
 template <typename T, int NJ>
 __global__ __launch_bounds__(256) void fold_norm_kernel(float* x, int Rin, int Kout, const T* g,
-                                                        float eps, int d, T* h,
-                                                        const float* part, int splits,
-                                                        int Mtot) {
+                                                        float eps, int d, T* h, PartView pv) {
   __shared__ float red[4];
   const int j0 = blockIdx.x;
-  const int64_t in_row = (int64_t)(j0 / Kout) * Rin + (j0 % Kout);
-  float* xr = x + in_row * d;
-  const int64_t stride = (int64_t)Mtot * d;
-  const float* pr = part + in_row * d;
+  const int in_row = (j0 / Kout) * Rin + (j0 % Kout);
+  float* xr = x + (int64_t)in_row * d;
+  const int64_t stride = pv.split_stride();
   float4 v[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) v[j] = *reinterpret_cast<const float4*>(xr + 4 * threadIdx.x + 1024 * j);
-  for (int s0 = 0; s0 < splits; s0 += 4) {
-    float4 pv[4][NJ];
+  for (int s0 = 0; s0 < pv.splits; s0 += 4) {
+    float4 pvv[4][NJ];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        pv[u][j] = (s0 + u < splits)
-            ? *reinterpret_cast<const float4*>(pr + (s0 + u) * stride + 4 * threadIdx.x + 1024 * j)
+        pvv[u][j] = (s0 + u < pv.splits)
+            ? *reinterpret_cast<const float4*>(pv.p + (s0 + u) * stride +
+                                               pv.off(in_row, 4 * threadIdx.x + 1024 * j))
             : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (s0 + u < splits)
+      if (s0 + u < pv.splits)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
-          v[j].x += pv[u][j].x; v[j].y += pv[u][j].y; v[j].z += pv[u][j].z; v[j].w += pv[u][j].w;
+          v[j].x += pvv[u][j].x; v[j].y += pvv[u][j].y; v[j].z += pvv[u][j].z; v[j].w += pvv[u][j].w;
         }
   }
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-    if (splits > 0) *reinterpret_cast<float4*>(xr + 4 * threadIdx.x + 1024 * j) = v[j];
+    if (pv.splits > 0) *reinterpret_cast<float4*>(xr + 4 * threadIdx.x + 1024 * j) = v[j];
   }
   ss = wave_sum(ss);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -123,19 +121,17 @@ __global__ __launch_bounds__(256) void fold_norm_kernel(float* x, int Rin, int K
 
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, int Rin, int Kout, const T* g,
-                                                      float eps, int d, T* h, const float* part,
-                                                      int splits, int Mtot) {
+                                                      float eps, int d, T* h, PartView pv) {
   __shared__ float red[4];
   int j = blockIdx.x;
-  int64_t in_row = (int64_t)(j / Kout) * Rin + (j % Kout);
-  float* xr = x + in_row * d;
-  if (splits > 0) {
+  const int in_row = (j / Kout) * Rin + (j % Kout);
+  float* xr = x + (int64_t)in_row * d;
+  if (pv.splits > 0) {
     // add the pending split-K partials of the residual GEMM, in split order
-    const float* pr = part + in_row * d;
-    const int64_t stride = (int64_t)Mtot * d;
+    const int64_t stride = pv.split_stride();
     for (int c = threadIdx.x; c < d; c += blockDim.x) {
       float v = xr[c];
-      for (int s = 0; s < splits; ++s) v += pr[s * stride + c];
+      for (int s = 0; s < pv.splits; ++s) v += pv.p[s * stride + pv.off(in_row, c)];
       xr[c] = v;
     }
     __syncthreads();
@@ -158,14 +154,12 @@ hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R,
 }
 
 hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
-                          float eps, int d, void* h, const float* part, int splits, int Mtot,
-                          hipStream_t st) {
+                          float eps, int d, void* h, const PartView& pv, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
   if (d % 1024 == 0 && d <= 8192) {
     const int nj = d / 1024;
 #define DLLM_FOLD(TT, NJV)                                                                  \
-  fold_norm_kernel<TT, NJV><<<rows, 256, 0, st>>>(x, Rin, Kout, (const TT*)g, eps, d, (TT*)h, \
-                                                  part, splits, Mtot)
+  fold_norm_kernel<TT, NJV><<<rows, 256, 0, st>>>(x, Rin, Kout, (const TT*)g, eps, d, (TT*)h, pv)
     if (dtype == F32) {
       switch (nj) { case 1: DLLM_FOLD(float, 1); break; case 2: DLLM_FOLD(float, 2); break;
                     case 4: DLLM_FOLD(float, 4); break; default: goto general; }
@@ -179,29 +173,31 @@ hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, cons
   }
 general:
   if (dtype == F32)
-    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, Rin, Kout, (const float*)g, eps, d, (float*)h,
-                                                part, splits, Mtot);
+    rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, Rin, Kout, (const float*)g, eps, d, (float*)h, pv);
   else
     rmsnorm_kernel<uint16_t><<<rows, 256, 0, st>>>(x, Rin, Kout, (const uint16_t*)g, eps, d,
-                                                   (uint16_t*)h, part, splits, Mtot);
+                                                   (uint16_t*)h, pv);
   return hipGetLastError();
 }
 
-__global__ void fold_partials_kernel(float* y, const float* part, int splits, int64_t n) {
+__global__ void fold_partials_kernel(float* y, PartView pv) {
+  const int64_t n = (int64_t)pv.M * pv.N;
+  const int64_t stride = pv.split_stride();
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / pv.N), c = (int)(i % pv.N);
     float v = y[i];
-    for (int s = 0; s < splits; ++s) v += part[s * n + i];
+    for (int s = 0; s < pv.splits; ++s) v += pv.p[s * stride + pv.off(m, c)];
     y[i] = v;
   }
 }
 
-hipError_t launch_fold_partials(float* y, const float* part, int splits, int64_t n,
-                                hipStream_t st) {
-  if (n <= 0) return hipSuccess;
+hipError_t launch_fold_partials(float* y, const PartView& pv, hipStream_t st) {
+  const int64_t n = (int64_t)pv.M * pv.N;
+  if (n <= 0 || pv.splits <= 0) return hipSuccess;
   int blocks = (int)((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  fold_partials_kernel<<<blocks, 256, 0, st>>>(y, part, splits, n);
+  fold_partials_kernel<<<blocks, 256, 0, st>>>(y, pv);
   return hipGetLastError();
 }
 

@@ -35,14 +35,42 @@ struct EpiArgs {
 
 enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2 };
 
+// Where split-K partial sums live.  Plain: [split][M][N].  Blocked (skinny GEMM): per split,
+// per 16-column group, one block of mrows x 16 floats in which row m, column c sits at
+// ((mt*4 + r)*4 + g)*16 + c with m = 16 mt + 4 g + r, so that every store instruction of
+// the producing wave writes 256 contiguous bytes.  Four consecutive columns starting at a
+// multiple of 4 are contiguous in both layouts.
+struct PartView {
+  const float* p = nullptr;
+  int splits = 0;
+  int blocked = 0;
+  int mrows = 0;        // blocked: rows per block (16, 32 or 64)
+  int M = 0, N = 0;     // plain: row stride is N
+  __host__ __device__ int64_t split_stride() const {
+    return blocked ? (int64_t)((N + 15) / 16) * mrows * 16 : (int64_t)M * N;
+  }
+  __host__ __device__ int64_t off(int m, int c) const {
+    if (!blocked) return (int64_t)m * N + c;
+    const int mt = m >> 4, g = (m & 15) >> 2, r = m & 3;
+    return (int64_t)(c >> 4) * mrows * 16 + ((mt * 4 + r) * 4 + g) * 16 + (c & 15);
+  }
+};
+
 struct GemmPlan {
   int kind = 0;
-  int mt = 1;            // skinny: 32-row tiles per workgroup (1 or 2)
+  int mt = 1;            // skinny: 16-row MFMA tiles per workgroup (1, 2 or 4)
   int ntn = 0, ntm = 0;  // tiles along N (virtual) and M
   int splits = 1, kchunk = 0;
   size_t part_floats = 0;  // split-K partial buffer
   int counters = 0;        // split-K arrival counters
   bool deferred = false;   // residual partials left for the next RMSNorm to add
+  PartView view(const float* part, int M, int N) const {
+    PartView v;
+    v.p = part; v.splits = splits; v.M = M; v.N = N;
+    v.blocked = (kind == GEMM_SKINNY);
+    v.mrows = mt * 16;
+    return v;
+  }
 };
 
 GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi);
@@ -82,14 +110,12 @@ hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R,
                              const void* embed, const void* g, float eps, int d, int V, float* x,
                              void* h, hipStream_t st);
 // h[j] = rmsnorm(x[in_row(j)]) * g, in_row(j) = (j / Kout) * Rin + j % Kout, j < rows.
-// With splits > 0, first x[in_row] += part[0][in_row] + ... + part[splits-1][in_row]
-// (part is [splits][Mtot][d] fp32, written back into x).
+// With pv.splits > 0, first x[in_row] += the pending split partials of that row (split
+// order), written back into x.
 hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
-                          float eps, int d, void* h, const float* part, int splits, int Mtot,
-                          hipStream_t st);
-// y[i] += part[0][i] + ... + part[splits-1][i], i < n  (n = M * N)
-hipError_t launch_fold_partials(float* y, const float* part, int splits, int64_t n,
-                                hipStream_t st);
+                          float eps, int d, void* h, const PartView& pv, hipStream_t st);
+// y[m][c] += sum over splits of the partials at (m, c), in split order (y is [M][N] fp32)
+hipError_t launch_fold_partials(float* y, const PartView& pv, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st);
 hipError_t launch_synth_fill(void* dst, int64_t n, int dtype, uint64_t seed, uint32_t tid,
                              double stdv, int mode, hipStream_t st);

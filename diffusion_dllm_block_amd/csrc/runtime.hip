@@ -222,7 +222,7 @@ dllm_status check_buffers(const Dims& d, const dllm_seq_desc* s, Ws* w) {
 // ------------------------------------------------------------------ execution
 struct Pending {  // split-K partials of a residual GEMM not yet added into x
   int splits = 0;
-  int M = 0;
+  PartView view;
 };
 
 struct Ctx {
@@ -254,7 +254,7 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
                       c.at<int>(c.w.gcnt), c.st));
   if (p.deferred && epi == EPI_RESID) {
     c.pend.splits = p.splits;
-    c.pend.M = M;
+    c.pend.view = p.view(c.at<float>(c.w.gpart), M, Nv);
   }
   return DLLM_OK;
 }
@@ -262,9 +262,10 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
 // RMSNorm of `rows` rows of x into h (see launch_rmsnorm); adds pending residual partials.
 dllm_status norm(const Ctx& c, int rows, int Rin, int Kout, const void* g) {
   ProfScope ps(DLLM_K_RMSNORM, c.st);
+  PartView pv = c.pend.view;
+  pv.splits = c.pend.splits;
   HIP_TRY(launch_rmsnorm(c.d.dtype, c.at<float>(c.w.x), rows, Rin, Kout, g, c.d.eps, c.d.d,
-                         c.at<void>(c.w.h), c.at<float>(c.w.gpart), c.pend.splits, c.pend.M,
-                         c.st));
+                         c.at<void>(c.w.h), pv, c.st));
   c.pend = Pending{};
   return DLLM_OK;
 }
@@ -596,8 +597,7 @@ dllm_status dllm_kernel_linear(const void* x, const void* w, void* y, int32_t M,
   EpiArgs e;
   e.y = y; e.ldy = N; e.scale = scale;
   HIP_TRY(launch_gemm(dtype, epi, p, x, K, w, M, N, K, e, part, cnt, st));
-  if (p.deferred && epi == EPI_RESID)
-    HIP_TRY(launch_fold_partials((float*)y, part, p.splits, (int64_t)M * N, st));
+  if (p.deferred && epi == EPI_RESID) HIP_TRY(launch_fold_partials((float*)y, p.view(part, M, N), st));
   return DLLM_OK;
 }
 
