@@ -158,6 +158,98 @@ def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int):
     }
 
 
+def _graph_time(torch, launch_all, n_launch: int, rounds: int) -> float:
+    """Average microseconds per launch of a sequence of launches captured once into a
+    HIP graph and replayed back to back (no host launch cost inside the timed region)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        launch_all()                     # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch_all()
+    g.replay()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for _ in range(rounds):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (rounds * n_launch)
+
+
+def kernel_only(lib, torch, bd, rounds: int = 10):
+    """Kernel-only workload at the 8B step shape: block attention of 32 query rows per
+    head (32 heads x 128) against 1024 cached keys, and the confidence/unmask pass over
+    [32, 126464] bf16 logits (N(0,1) plus a U(0,12) boost at one id per row, tau 0.9,
+    all 32 positions masked).  Launches rotate through buffer sets totalling more than
+    the 256 MB Infinity Cache and are replayed from a HIP graph; the time per launch is
+    HIP events around the replays divided by the launches (so it includes the short gaps
+    between kernels, and for the confidence entry its counter-reset kernel)."""
+    out = {}
+    # ---- attention
+    B, Hq, Hkv, R, S, D = 1, 32, 32, 32, 1024, 128
+    Sp = (S + 63) // 64 * 64
+    nset = 20
+    sets = []
+    st0 = bd.stream_handle()
+    for i in range(nset):
+        t = {}
+        for name, n, tid in (("q", B * Hq * R * D, 0xA100), ("k", B * Hkv * Sp * D, 0xA101),
+                             ("vt", B * Hkv * D * Sp, 0xA102)):
+            t[name] = torch.empty(n, dtype=torch.int16, device="cuda")
+            lib.call("dllm_synth_fill", bd.ptr(t[name]), n, 1, 42 + i, tid, 1.0, 0, st0)
+        t["o"] = torch.empty(B * R * Hq * D, dtype=torch.int16, device="cuda")
+        sets.append(t)
+    wsb = lib.raw("dllm_kernel_workspace_bytes")(B, Hq, R, S, D, 0, 0)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def attn_all():
+        st = bd.stream_handle()
+        for t in sets:
+            lib.call("dllm_kernel_block_attention", bd.ptr(t["q"]), bd.ptr(t["k"]),
+                     bd.ptr(t["vt"]), bd.ptr(t["o"]), B, Hq, Hkv, R, S, Sp, D, 1, bd.ptr(ws),
+                     wsb, st)
+    us = _graph_time(torch, attn_all, nset, rounds)
+    nbytes = (B * Hq * R * D * 2) * 2 + B * Hkv * S * D * 2 * 2
+    out["attention"] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+                        "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "sets": nset,
+                        "shape": "B1 H32x128 q32 kv1024 bf16"}
+    del sets
+    # ---- confidence / unmask
+    K, V, mask_id, tau = 32, 126464, 126463, 0.9
+    host = synth.boosted_logits(43, K, V, 12.0, "bf16")
+    one = torch.from_numpy(host.view(np.int16)).to("cuda")
+    nset = 40
+    logits = [one.clone() for _ in range(nset)]
+    toks = torch.full((nset, K), mask_id, dtype=torch.int32, device="cuda")
+    conf = torch.empty(K, dtype=torch.float32, device="cuda")
+    arg = torch.empty(K, dtype=torch.int32, device="cuda")
+    nun = torch.empty(1, dtype=torch.int32, device="cuda")
+    rem = torch.empty(1, dtype=torch.int32, device="cuda")
+    uidx = torch.empty(K, dtype=torch.int32, device="cuda")
+    wsb = lib.raw("dllm_kernel_workspace_bytes")(1, 0, 0, 0, 0, K, V)
+    ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
+
+    def conf_all():
+        st = bd.stream_handle()
+        toks.fill_(mask_id)             # every launch sees a fully masked block
+        for i in range(nset):
+            lib.call("dllm_kernel_confidence_unmask", bd.ptr(logits[i]), 1, 1, K, V, mask_id,
+                     tau, bd.ptr(toks[i]), K, bd.ptr(conf), bd.ptr(arg), bd.ptr(nun),
+                     bd.ptr(rem), bd.ptr(uidx), bd.ptr(ws), wsb, st)
+    us = _graph_time(torch, conf_all, nset, rounds)
+    nbytes = K * V * 2
+    out["confidence"] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+                         "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "sets": nset,
+                         "shape": "[32, 126464] bf16 logits, tau 0.9"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +258,9 @@ def main():
     ap.add_argument("--workload", default="llada8b_dual_p1000_g1024")
     ap.add_argument("--gen-len", type=int, default=0, help="override (for quick runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernels", action="store_true", help="skip the kernel-only rates")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="only the kernel-only rates (no generation; for profiling)")
     ap.add_argument("--roofline-kernel", default="auto")
     ap.add_argument("--logit-scale", type=float, default=0.0,
                     help="override the calibrated scale (exploration only)")
@@ -180,6 +275,9 @@ def main():
     from diffusion_dllm_block_amd.engine import Model, Session
 
     lib = bd.load()
+    if a.kernels_only:
+        print(json.dumps({"kernels": kernel_only(lib, torch, bd)}), flush=True)
+        return
     wl = synth.with_scale(synth.WORKLOADS[a.workload],
                           a.logit_scale if a.logit_scale else logit_scale(a.workload))
     if a.gen_len:
@@ -251,6 +349,9 @@ def main():
                    "tokens_per_step": round(wl.batch * wl.gen_len / max(1, nfe_steps), 3)},
         "roofline": roof,
     }
+    if not a.no_kernels:
+        log("kernel-only rates (attention, confidence)")
+        out["kernels"] = kernel_only(lib, torch, bd)
     if not a.no_cpu_baseline:
         del sess, model
         torch.cuda.empty_cache()

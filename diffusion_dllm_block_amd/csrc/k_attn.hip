@@ -37,52 +37,61 @@ __device__ __forceinline__ bf16x8 pack_p(const float* p, int u) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// 4 bf16 at keys k..k+3 (k % 4 == 0) of a Vt row of stride Sp (Sp % 8 == 0, Sp >= S);
-// keys >= S read as zero.  Branch-free: the address is clamped inside the row and the
-// value masked, so the padding past S (never written) cannot leak in.
-__device__ __forceinline__ uint64_t load4_masked(const uint16_t* row, int k, int S, int Sp) {
-  const uint64_t v = *reinterpret_cast<const uint64_t*>(row + min(k, Sp - 4));
+// 8 bf16 at keys k..k+7 (k % 8 == 0) of a Vt row, one 16-byte load; keys >= S read as
+// zero (clamped address, masked value).
+__device__ __forceinline__ bf16x8 load8_masked(const uint16_t* row, int k, int S, int Sp) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(row + min(k, Sp - 8));
   const int n = S - k;
-  const uint64_t keep = n >= 4 ? ~0ull : (n <= 0 ? 0ull : (1ull << (16 * n)) - 1ull);
-  return v & keep;
-}
-
-// Vt operand for keys {16u + 4g + 0..3, 16u + 8 + 4g + 0..3} of a 32-key tile at key0,
-// row d; keys >= S read as zero.
-__device__ __forceinline__ bf16x8 load_vt(const uint16_t* vrow, int key0, int u, int g, int S,
-                                          int Sp) {
-  const int ka = key0 + 16 * u + 4 * g;
-  const uint64_t a = load4_masked(vrow, ka, S, Sp);
-  const uint64_t b = load4_masked(vrow, ka + 8, S, Sp);
-  u32x4 r = u32x4{(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
-  return as_bf16x8(r);
+  auto keep = [](int c) {  // c elements of 4 kept
+    return c >= 4 ? ~0ull : (c <= 0 ? 0ull : (1ull << (16 * c)) - 1ull);
+  };
+  const uint64_t lo = (((uint64_t)v[1] << 32) | v[0]) & keep(n);
+  const uint64_t hi = (((uint64_t)v[3] << 32) | v[2]) & keep(n - 4);
+  return as_bf16x8(u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
 }
 
 // ============================================================================
 // Split-KV attention for a few query rows (a block step): grid (nchunk, Hq*nqt, B),
-// 4 waves.  Chunk c covers keys [c*4*kpw, (c+1)*4*kpw); wave w walks its kpw keys in
-// 32-key sub-tiles with an online softmax, loading the next sub-tile's K and Vt while
-// the current one is in the MFMAs.  The 4 waves are merged in LDS; with several chunks
-// the workgroup writes unnormalised partials (O, m, l) and attn_combine merges them.
+// 4 waves, 32 query rows per workgroup.  Chunk c covers keys [c*4*kpw, (c+1)*4*kpw);
+// wave w walks its kpw keys in 32-key sub-tiles with an online softmax, loading the
+// next sub-tile while the current one is in the MFMAs.
+//
+// Products use v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, k 8(l/16)..+7; B column
+// l%16, same k; C column l%16, rows 4(l/16)+r), so every operand load is 4 lanes x 16
+// bytes = 64 contiguous bytes of one K row or one Vt row:
+//   S^T tile tau (16 keys x 16 queries) = K . Q^T over 4 k-steps of 32 dims; A row i of
+//       tile tau is key 8(i/4) + 4 tau + i%4 of the sub-tile, so lane group j = l/16
+//       ends up holding scores of keys 8j .. 8j+7 (tau 0: +0..3, tau 1: +4..7);
+//   O^T (16 dims x 16 queries) += Vt . P^T with k = the 32 keys in natural order: the
+//       lane's 8 scores are exactly its B operand, and the Vt operand of lane (d, j) is
+//       keys 8j .. 8j+7 of row d.
+// A query's 32 keys live in the 4 lanes l%16 + 16j, so its max and sum need two xor
+// shuffles.  Waves are merged through LDS in a fixed order; with several chunks the
+// workgroup writes unnormalised partials (O, m, l) and attn_combine merges them.
 // ============================================================================
-struct KVTile {
-  u32x4 k[8];       // K operand: key lr, d = 16t + 8g .. +8
-  bf16x8 v[4][2];   // Vt operands: d = 32dt + lr, keys of accumulator rows 8u .. 8u+7
+constexpr int SK_OLD = HD + 4;  // LDS row stride (floats) of the per-wave O tiles
+
+struct KVTile16 {
+  u32x4 k[2][4];  // [tau][k-step]: K row of key 8(i/4) + 4 tau + i%4, dims 32 s + 8j
+  u32x4 v[8];     // [d-tile]: Vt row 16 dt + l%16, keys 8j .. 8j+7
 };
 
-__device__ __forceinline__ void load_kv_tile(KVTile& t, const uint16_t* kbase,
-                                             const uint16_t* vbase, int key0, int lr, int g,
-                                             int S, int Sp) {
-  // keys >= S: any valid K row will do (their scores are masked to -inf)
-  const int key = min(key0 + lr, S - 1);
-  const uint16_t* kp = kbase + (int64_t)key * HD + 8 * g;
+__device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
+                                          const uint16_t* vbase, int key0, int li, int j, int S,
+                                          int Sp) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t.k[i] = *reinterpret_cast<const u32x4*>(kp + 16 * i);
+  for (int tau = 0; tau < 2; ++tau) {
+    // keys >= S: any valid K row will do (their scores are masked to -inf)
+    const int key = min(key0 + 8 * (li >> 2) + 4 * tau + (li & 3), S - 1);
+    const uint16_t* kp = kbase + (int64_t)key * HD + 8 * j;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int st = 0; st < 4; ++st) t.k[tau][st] = *reinterpret_cast<const u32x4*>(kp + 32 * st);
+  }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      t.v[dt][u] = load_vt(vbase + (int64_t)(32 * dt + lr) * Sp, key0, u, g, S, Sp);
+  for (int dt = 0; dt < 8; ++dt) {
+    const bf16x8 v = load8_masked(vbase + (int64_t)(16 * dt + li) * Sp, key0 + 8 * j, S, Sp);
+    t.v[dt] = __builtin_bit_cast(u32x4, v);
+  }
 }
 
 __global__ __launch_bounds__(256) void attn_splitkv_bf16(
@@ -91,112 +100,149 @@ __global__ __launch_bounds__(256) void attn_splitkv_bf16(
     int Sp, int nqt, int nchunk, int nsub, float scale_log2, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
   __shared__ float red_m[4][32], red_l[4][32];
-  __shared__ float osum[HD][33];
+  __shared__ __attribute__((aligned(16))) float osum[4][32][SK_OLD];
   const int chunk = blockIdx.x;
   const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
   const int hkv = hq / (Hq / Hkv);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, lr = l & 31, g = l >> 5;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, j = l >> 4;
   const int kpw = 32 * nsub;
   const int wkey0 = chunk * 4 * kpw + w * kpw;
 
-  // Q^T operand: lane (query lr, half g) holds Q[row][16t + 8g .. +8]
-  const int qrow = min(qt * 32 + lr, R - 1);  // rows >= R: computed, never stored
-  const uint16_t* qp = q + (((int64_t)b * Hq + hq) * R + qrow) * HD + 8 * g;
-  u32x4 qf[8];
+  // Q^T operands: [query tile qq][k-step]: query 16 qq + li, dims 32 s + 8j .. +8
+  u32x4 qf[2][4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) qf[t] = *reinterpret_cast<const u32x4*>(qp + 16 * t);
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qrow = min(qt * 32 + 16 * qq + li, R - 1);  // rows >= R: computed, never stored
+    const uint16_t* qp = q + (((int64_t)b * Hq + hq) * R + qrow) * HD + 8 * j;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) qf[qq][st] = *reinterpret_cast<const u32x4*>(qp + 32 * st);
+  }
   const uint16_t* kbase = k + ((int64_t)b * Hkv + hkv) * Sp * HD;
   const uint16_t* vbase = vt + ((int64_t)b * Hkv + hkv) * HD * Sp;
 
-  f32x16 oacc[4];
+  f32x4 oacc[2][8];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[qq][dt] = f32x4{};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-  auto consume = [&](const KVTile& t, int key0) {
-    f32x16 s = {};
+  auto consume = [&](const KVTile16& t, int key0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s = mfma32(as_bf16x8(t.k[i]), as_bf16x8(qf[i]), s);
-    float p[16];
-    float mx = -INFINITY;
+    for (int qq = 0; qq < 2; ++qq) {
+      f32x4 sc[2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      float x = (key0 + acc_row(v, g) < S) ? s[v] * scale_log2 : -INFINITY;
-      p[v] = x;
-      mx = fmaxf(mx, x);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    if (m_new == -INFINITY) return;  // no valid key yet for this wave
-    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float ls = 0.f;
+      for (int tau = 0; tau < 2; ++tau) {
+        sc[tau] = f32x4{};
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      p[v] = __builtin_amdgcn_exp2f(p[v] - m_new);
-      ls += p[v];
-    }
-    ls += __shfl_xor(ls, 32, kWave);
-    l_run = l_run * alpha + ls;
-    m_run = m_new;
+        for (int st = 0; st < 4; ++st)
+          sc[tau] = mfma16(as_bf16x8(t.k[tau][st]), as_bf16x8(qf[qq][st]), sc[tau]);
+      }
+      // lane's 8 scores: keys key0 + 8j + e, e = 4 tau + r
+      float p[8];
+      float mx = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      oacc[dt] *= alpha;
+      for (int e = 0; e < 8; ++e) {
+        const float x = (key0 + 8 * j + e < S) ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+        p[e] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[qq], mx);
+      // a sub-tile with no valid key at all leaves the state unchanged
+      const float alpha = (m_new == -INFINITY || m_run[qq] == -INFINITY)
+                              ? ((m_new == -INFINITY) ? 1.f : 0.f)
+                              : __builtin_amdgcn_exp2f(m_run[qq] - m_new);
+      float ls = 0.f;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) oacc[dt] = mfma32(t.v[dt][u], pack_p(p, u), oacc[dt]);
+      for (int e = 0; e < 8; ++e) {
+        p[e] = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[e] - m_new);
+        ls += p[e];
+      }
+      ls += __shfl_xor(ls, 16, kWave);
+      ls += __shfl_xor(ls, 32, kWave);
+      l_run[qq] = l_run[qq] * alpha + ls;
+      m_run[qq] = m_new;
+      u16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = f2bf(p[e]);
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, pb);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        oacc[qq][dt] *= alpha;
+        oacc[qq][dt] = mfma16(as_bf16x8(t.v[dt]), pop, oacc[qq][dt]);
+      }
     }
   };
 
-  KVTile ta, tb;
-  load_kv_tile(ta, kbase, vbase, wkey0, lr, g, S, Sp);
-  for (int j = 0; j < nsub; j += 2) {
-    if (j + 1 < nsub) load_kv_tile(tb, kbase, vbase, wkey0 + 32 * (j + 1), lr, g, S, Sp);
-    consume(ta, wkey0 + 32 * j);
-    if (j + 1 >= nsub) break;
-    if (j + 2 < nsub) load_kv_tile(ta, kbase, vbase, wkey0 + 32 * (j + 2), lr, g, S, Sp);
-    consume(tb, wkey0 + 32 * (j + 1));
+  KVTile16 ta, tb;
+  load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
+  for (int n = 0; n < nsub; n += 2) {
+    if (n + 1 < nsub) load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
+    consume(ta, wkey0 + 32 * n);
+    if (n + 1 >= nsub) break;
+    if (n + 2 < nsub) load_kv16(ta, kbase, vbase, wkey0 + 32 * (n + 2), li, j, S, Sp);
+    consume(tb, wkey0 + 32 * (n + 1));
   }
 
   // ---- merge the 4 waves (fixed order)
-  if (g == 0) { red_m[w][lr] = m_run; red_l[w][lr] = l_run; }
-  __syncthreads();
-  float M = red_m[0][lr];
-  for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i][lr]);
-  float L = 0.f;
-  for (int i = 0; i < 4; ++i)
-    L += (red_m[i][lr] == -INFINITY) ? 0.f : red_l[i][lr] * __builtin_amdgcn_exp2f(red_m[i][lr] - M);
-  const float f = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
+  if (j == 0) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          int d = 32 * dt + acc_row(v, g);
-          float val = oacc[dt][v] * f;
-          osum[d][lr] = (ww == 0) ? val : osum[d][lr] + val;
-        }
-    }
-    __syncthreads();
+    for (int qq = 0; qq < 2; ++qq) { red_m[w][16 * qq + li] = m_run[qq]; red_l[w][16 * qq + li] = l_run[qq]; }
   }
-  // L and M per query are identical in every wave; publish them through LDS
-  if (w == 0 && g == 0) { red_m[0][lr] = M; red_l[0][lr] = L; }
   __syncthreads();
-
-  if (nchunk == 1) {
-    for (int e = threadIdx.x; e < 32 * HD; e += blockDim.x) {
-      int qi = e / HD, d = e % HD;
-      int row = qt * 32 + qi;
-      if (row < R)
-        o[((int64_t)b * R + row) * (Hq * HD) + hq * HD + d] = f2bf(osum[d][qi] / red_l[0][qi]);
+  // this wave's O scaled to the workgroup maximum: lane holds query 16 qq + li,
+  // dims 16 dt + 4j + r
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qi = 16 * qq + li;
+    float M = red_m[0][qi];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i][qi]);
+    const float f = (m_run[qq] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qq] - M);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float4 val = make_float4(oacc[qq][dt][0] * f, oacc[qq][dt][1] * f, oacc[qq][dt][2] * f,
+                               oacc[qq][dt][3] * f);
+      *reinterpret_cast<float4*>(&osum[w][qi][16 * dt + 4 * j]) = val;
     }
-    return;
   }
+  __syncthreads();
+  // thread -> (query qi, dims 4 d4 .. +4) for 4 (query, d4) pairs; waves summed in order
   const int64_t grp = ((int64_t)b * Hq + hq) * nqt + qt;
-  float* po = part_o + (grp * nchunk + chunk) * (32 * HD);
-  for (int e = threadIdx.x; e < 32 * HD; e += blockDim.x) po[e] = osum[e % HD][e / HD];
-  if (threadIdx.x < 64) {
-    float* pml = part_ml + (grp * nchunk + chunk) * 64;
-    pml[threadIdx.x] = threadIdx.x < 32 ? red_m[0][threadIdx.x] : red_l[0][threadIdx.x - 32];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int e = threadIdx.x + 256 * it;
+    const int qi = e >> 5, d4 = (e & 31) * 4;
+    float4 acc = *reinterpret_cast<const float4*>(&osum[0][qi][d4]);
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+      const float4 u = *reinterpret_cast<const float4*>(&osum[ww][qi][d4]);
+      acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+    }
+    float M = red_m[0][qi];
+    for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i][qi]);
+    float L = 0.f;
+    for (int i = 0; i < 4; ++i)
+      L += (red_m[i][qi] == -INFINITY) ? 0.f : red_l[i][qi] * __builtin_amdgcn_exp2f(red_m[i][qi] - M);
+    if (nchunk == 1) {
+      const int row = qt * 32 + qi;
+      if (row < R) {
+        const float inv = 1.0f / L;
+        u16x4 r;
+        r[0] = f2bf(acc.x * inv); r[1] = f2bf(acc.y * inv); r[2] = f2bf(acc.z * inv); r[3] = f2bf(acc.w * inv);
+        *reinterpret_cast<u16x4*>(o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD + d4) = r;
+      }
+    } else {
+      float* po = part_o + (grp * nchunk + chunk) * (32 * HD);
+      *reinterpret_cast<float4*>(po + qi * HD + d4) = acc;
+      if (d4 == 0) {
+        float* pml = part_ml + (grp * nchunk + chunk) * 64;
+        pml[qi] = M;
+        pml[32 + qi] = L;
+      }
+    }
   }
 }
 

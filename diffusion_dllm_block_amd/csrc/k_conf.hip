@@ -6,13 +6,14 @@
 // (ccyt168.com Fast-dLLM article, section 1.2 "Confidence-Aware Parallel Decoding";
 // techwalker.com explainer, "Solving the quality loss of parallel decoding").
 //
-// Layout of the work: grid (nsplit, rows).  Each workgroup streams one slice of one row
+// Two passes.  Pass 1, grid (nsplit, rows): each workgroup streams one slice of one row
 // with 16-byte loads and keeps a per-thread online (max, argmax, sum exp) triple; the
 // triples are merged in a fixed order (thread-sequential, wave butterfly, waves in
-// order) into a per-(row, slice) partial.  The last workgroup of a sequence to finish
-// (device-scope arrival counter) merges the slices of its K rows in slice order, one
-// lane per row, and runs the unmask rule with wave ballots.  No float atomics: results
-// are bit-identical from run to run.
+// order) into a per-(row, slice) partial.  Pass 2, one workgroup per sequence, merges
+// each row's slices in slice order (one lane per row) and runs the unmask rule with
+// wave ballots.  No atomics: results are bit-identical from run to run.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -96,52 +97,91 @@ __device__ __forceinline__ Trip wave_merge(Trip t) {
   return t;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void conf_unmask_kernel(
-    const T* __restrict__ logits, int B, int K, int V, int mask_id, float tau, int nsplit,
-    int chunk, int* tokens, int ld_tokens, float* conf, int* argmax, int* n_unmasked,
-    int* remaining, int* unmasked_idx, float* pm, float* ps, int* pi, int* counters) {
-  __shared__ Trip red[4];
-  __shared__ int flag;
+constexpr int kConfThreads = 256;
+constexpr int kConfMaxParts = 2048;  // K * nsplit per sequence (finalize stages them in LDS)
+constexpr int kConfMaxSplit = 64;
+
+// Pass 1, one workgroup per (slice, row).  A slice is IT * 2048 consecutive ids (the
+// last one shorter); each thread issues all of its IT 8-element loads before folding
+// them, so a slice costs one memory round trip.  Writes the slice's (max, sum, argmax).
+template <typename T, int IT>
+__global__ __launch_bounds__(kConfThreads) void conf_partials_kernel(
+    const T* __restrict__ logits, int V, int mask_id, int nsplit, int chunk, float* pm,
+    float* ps, int* pi) {
+  __shared__ Trip red[kConfThreads / kWave];
   const int split = blockIdx.x, row = blockIdx.y;
   const int lo = split * chunk;
   const int hi = min(V, lo + chunk);
   const T* zr = logits + (int64_t)row * V;
+  const int tid = threadIdx.x;
 
   Trip t{-INFINITY, 0.f, 0x7fffffff};
-  const bool vec = (V % 8) == 0;  // rows and slices start on 16-byte boundaries
-  if (vec) {
-    for (int i = lo + threadIdx.x * 8; i < hi; i += blockDim.x * 8) {
-      float v[8];
-      load8<T>(zr + i, v);
-      fold(t, v, 8, i, mask_id);
+  if ((V % 8) == 0) {  // rows and slices start on 16-byte boundaries
+    for (int base = lo; base < hi; base += IT * kConfThreads * 8) {
+      float v[IT][8];
+#pragma unroll
+      for (int j = 0; j < IT; ++j)  // clamped in-row address; values past hi are dropped
+        load8<T>(zr + min(base + (j * kConfThreads + tid) * 8, V - 8), v[j]);
+#pragma unroll
+      for (int j = 0; j < IT; ++j) {
+        const int i = base + (j * kConfThreads + tid) * 8;
+        fold(t, v[j], min(max(hi - i, 0), 8), i, mask_id);
+      }
     }
   } else {
-    for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) {
+    for (int i = lo + tid; i < hi; i += kConfThreads) {
       float v[8];
       v[0] = Elt<T>::load(zr, i);
       fold(t, v, 1, i, mask_id);
     }
   }
   t = wave_merge(t);
-  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int w = tid / kWave, lane = tid % kWave;
   if (lane == 0) red[w] = t;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     Trip a = red[0];
-    for (int i = 1; i < (int)(blockDim.x / kWave); ++i) a = merge(a, red[i]);
-    int64_t o = (int64_t)row * nsplit + split;
-    st_dev(&pm[o], a.m);
-    st_dev(&ps[o], a.s);
-    st_dev(&pi[o], a.idx);
+    for (int i = 1; i < kConfThreads / kWave; ++i) a = merge(a, red[i]);
+    const int64_t o = (int64_t)row * nsplit + split;
+    pm[o] = a.m;
+    ps[o] = a.s;
+    pi[o] = a.idx;
   }
+}
 
-  const int b = row / K;
-  if (!arrive_last(&counters[b], K * nsplit, &flag)) return;
-  if (threadIdx.x >= kWave) return;
+// Pass 2, one workgroup per sequence: stage its K * nsplit partials in LDS (all loads
+// issued together), merge each row's slices in slice order (lane i of wave 0 = block
+// position i), then apply the threshold rule with wave ballots.
+__global__ __launch_bounds__(kConfThreads) void conf_finalize_kernel(
+    int K, int nsplit, int mask_id, float tau, const float* pm, const float* ps, const int* pi,
+    int* tokens, int ld_tokens, float* conf, int* argmax, int* n_unmasked, int* remaining,
+    int* unmasked_idx) {
+  __shared__ float fm[kConfMaxParts], fs[kConfMaxParts];
+  __shared__ int fi[kConfMaxParts];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nparts = K * nsplit;
+  const int64_t pbase = (int64_t)b * K * nsplit;
+  for (int e0 = 0; e0 < nparts; e0 += kConfThreads * 8) {
+    float lm[8], ls[8];
+    int li[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = min(e0 + u * kConfThreads + tid, nparts - 1);
+      lm[u] = pm[pbase + e];
+      ls[u] = ps[pbase + e];
+      li[u] = pi[pbase + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = e0 + u * kConfThreads + tid;
+      if (e < nparts) { fm[e] = lm[u]; fs[e] = ls[u]; fi[e] = li[u]; }
+    }
+  }
+  __syncthreads();
+  if (tid >= kWave) return;
 
-  // ---- finalize sequence b: lane i handles block position i (K <= 64)
-  const int i = lane;
+  const int i = tid;
   const bool active = i < K;
   float c = 0.f;
   int am = 0;
@@ -149,9 +189,8 @@ __global__ __launch_bounds__(256) void conf_unmask_kernel(
     const int r = b * K + i;
     Trip a{-INFINITY, 0.f, 0x7fffffff};
     for (int sp = 0; sp < nsplit; ++sp) {
-      int64_t o = (int64_t)r * nsplit + sp;
-      Trip u{ld_dev(&pm[o]), ld_dev(&ps[o]), ld_dev(&pi[o])};
-      a = merge(a, u);
+      const int e = i * nsplit + sp;
+      a = merge(a, Trip{fm[e], fs[e], fi[e]});
     }
     c = 1.0f / a.s;
     am = a.idx;
@@ -179,49 +218,70 @@ __global__ __launch_bounds__(256) void conf_unmask_kernel(
   }
   if (pick) tb[i] = am;
   const int nsel = __popcll(ballot_sel);
-  if (lane == 0) {
+  if (i == 0) {
     n_unmasked[b] = nsel;
     remaining[b] = __popcll(ballot_masked) - nsel;
   }
   if (unmasked_idx != nullptr && active) {
-    const uint64_t below = ballot_sel & ((1ull << lane) - 1ull);
+    const uint64_t below = ballot_sel & ((1ull << i) - 1ull);
     if (pick) unmasked_idx[b * K + __popcll(below)] = i;
     if (i >= nsel) unmasked_idx[b * K + i] = -1;
   }
 }
 
+// Slices of IT * 2048 ids with IT in {1, 2, 4, 8}: about 1024 workgroups in total, at
+// most kConfMaxSplit slices per row and kConfMaxParts partials per sequence.
 ConfPlan conf_plan(int rows, int V, int B) {
   ConfPlan p;
-  int target = 512;
-  int ns = (target + rows - 1) / rows;
-  int maxs = (V + 2047) / 2048;  // keep >= 2048 values per slice
-  if (ns > maxs) ns = maxs;
-  if (ns < 1) ns = 1;
-  int chunk = (V + ns - 1) / ns;
-  chunk = (chunk + 7) / 8 * 8;
-  ns = (V + chunk - 1) / chunk;
+  const int K = rows / (B > 0 ? B : 1);
+  const int per = kConfThreads * 8;
+  int want = (1024 + rows - 1) / rows;  // slices per row for ~1024 workgroups
+  if (want < 1) want = 1;
+  int it = 1;
+  while (it < 8 && (int64_t)it * per * want < V) it *= 2;
+  int chunk = it * per;
+  int ns = (V + chunk - 1) / chunk;
+  const int cap = std::min(kConfMaxSplit, kConfMaxParts / (K > 0 ? K : 1));
+  if (ns > cap) {  // very large vocabularies: longer slices (looped inside the kernel)
+    chunk = ((V + cap - 1) / cap + per - 1) / per * per;
+    ns = (V + chunk - 1) / chunk;
+  }
+  p.it = it;
   p.nsplit = ns;
   p.chunk = chunk;
   p.part_elems = (size_t)rows * ns;
-  p.counters = B;
   return p;
 }
 
 hipError_t launch_conf_unmask(int ldtype, const ConfPlan& p, const void* logits, int B, int K,
                               int V, int mask_id, float tau, int* tokens, int ld_tokens,
                               float* conf, int* argmax, int* n_unmasked, int* remaining,
-                              int* unmasked_idx, float* pm, float* ps, int* pi, int* counters,
-                              hipStream_t st) {
+                              int* unmasked_idx, float* pm, float* ps, int* pi, hipStream_t st) {
   if (B <= 0 || K <= 0) return hipSuccess;
+  if (K > kWave || K * p.nsplit > kConfMaxParts) return hipErrorInvalidValue;
   dim3 grid(p.nsplit, B * K);
-  if (ldtype == F32)
-    conf_unmask_kernel<float><<<grid, 256, 0, st>>>(
-        (const float*)logits, B, K, V, mask_id, tau, p.nsplit, p.chunk, tokens, ld_tokens, conf,
-        argmax, n_unmasked, remaining, unmasked_idx, pm, ps, pi, counters);
-  else
-    conf_unmask_kernel<uint16_t><<<grid, 256, 0, st>>>(
-        (const uint16_t*)logits, B, K, V, mask_id, tau, p.nsplit, p.chunk, tokens, ld_tokens,
-        conf, argmax, n_unmasked, remaining, unmasked_idx, pm, ps, pi, counters);
+#define DLLM_CONF(TT, ITV)                                                                  \
+  conf_partials_kernel<TT, ITV><<<grid, kConfThreads, 0, st>>>((const TT*)logits, V, mask_id, \
+                                                               p.nsplit, p.chunk, pm, ps, pi)
+#define DLLM_CONF_IT(TT)                  \
+  switch (p.it) {                         \
+    case 1: DLLM_CONF(TT, 1); break;      \
+    case 2: DLLM_CONF(TT, 2); break;      \
+    case 4: DLLM_CONF(TT, 4); break;      \
+    default: DLLM_CONF(TT, 8); break;     \
+  }
+  if (ldtype == F32) {
+    DLLM_CONF_IT(float)
+  } else {
+    DLLM_CONF_IT(uint16_t)
+  }
+#undef DLLM_CONF_IT
+#undef DLLM_CONF
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  conf_finalize_kernel<<<B, kConfThreads, 0, st>>>(K, p.nsplit, mask_id, tau, pm, ps, pi, tokens,
+                                                   ld_tokens, conf, argmax, n_unmasked,
+                                                   remaining, unmasked_idx);
   return hipGetLastError();
 }
 

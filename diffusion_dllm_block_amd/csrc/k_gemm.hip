@@ -214,10 +214,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   u32x4 wr[C::NLOAD];
   {
+    // issued in t order, like the refills in the loop, so that the loop's wait counts
+    // are the same on entry and on the back edge (otherwise the compiler falls back to
+    // waiting for every load at the top of each group)
     const uint16_t* wp = wptr(grp0);
 #pragma unroll
-    for (int t = 0; t < C::NLOAD; ++t)
+    for (int t = 0; t < C::NLOAD; ++t) {
       wr[t] = *reinterpret_cast<const u32x4*>(wp + 32 * t);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   for (int grp = grp0; grp < ngrp; grp += nw * 8) {

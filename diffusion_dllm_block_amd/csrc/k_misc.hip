@@ -64,33 +64,43 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const int* tokens, int 
   rms_row<T>(xr, g, eps, d, h + (int64_t)j * d, red);
 }
 
-// Single pass, the row held in registers: thread t owns columns 4t + 1024j (float4).
-// x = x + part[0] + ... + part[splits-1] (split order), written back; then
-// h = x / sqrt(mean(x^2) + eps) * g.  All loads of a thread are issued before the first
-// use.  Needs d % 1024 == 0 and d <= 8192 (the general kernel above covers the rest).
-template <typename T, int NJ>
-__global__ __launch_bounds__(256) void fold_norm_kernel(float* x, int Rin, int Kout, const T* g,
-                                                        float eps, int d, T* h, PartView pv) {
-  __shared__ float red[4];
+// Single pass, the row held in registers: 1024 threads, thread t owns the float4 columns
+// 4t + 4096j (j < NJ; columns >= d are skipped).  x = x + part[0] + ... + part[splits-1]
+// (split order), written back; then h = x / sqrt(mean(x^2) + eps) * g.  The loads of up
+// to G splits are all issued before the first add, so a typical fold is one memory
+// round trip.  Needs d % 4 == 0 and d <= 4096 * NJ.
+constexpr int kFoldThreads = 1024;
+template <typename T, int NJ, int G>
+__global__ __launch_bounds__(kFoldThreads) void fold_norm_kernel(float* x, int Rin, int Kout,
+                                                                const T* g, float eps, int d,
+                                                                T* h, PartView pv) {
+  __shared__ float red[kFoldThreads / kWave];
   const int j0 = blockIdx.x;
   const int in_row = (j0 / Kout) * Rin + (j0 % Kout);
   float* xr = x + (int64_t)in_row * d;
   const int64_t stride = pv.split_stride();
+  const int tid = threadIdx.x;
   float4 v[NJ];
+  bool ok[NJ];
+  int col[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) v[j] = *reinterpret_cast<const float4*>(xr + 4 * threadIdx.x + 1024 * j);
-  for (int s0 = 0; s0 < pv.splits; s0 += 4) {
-    float4 pvv[4][NJ];
+  for (int j = 0; j < NJ; ++j) {
+    col[j] = 4 * tid + 4096 * j;
+    ok[j] = col[j] < d;
+    col[j] = ok[j] ? col[j] : 0;  // clamped, never stored
+    v[j] = *reinterpret_cast<const float4*>(xr + col[j]);
+  }
+  for (int s0 = 0; s0 < pv.splits; s0 += G) {
+    float4 pvv[G][NJ];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < G; ++u) {
+      const int sp = min(s0 + u, pv.splits - 1);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
-        pvv[u][j] = (s0 + u < pv.splits)
-            ? *reinterpret_cast<const float4*>(pv.p + (s0 + u) * stride +
-                                               pv.off(in_row, 4 * threadIdx.x + 1024 * j))
-            : make_float4(0.f, 0.f, 0.f, 0.f);
+        pvv[u][j] = *reinterpret_cast<const float4*>(pv.p + sp * stride + pv.off(in_row, col[j]));
+    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < G; ++u)
       if (s0 + u < pv.splits)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -100,18 +110,22 @@ __global__ __launch_bounds__(256) void fold_norm_kernel(float* x, int Rin, int K
   float ss = 0.f;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
+    if (!ok[j]) continue;
     ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-    if (pv.splits > 0) *reinterpret_cast<float4*>(xr + 4 * threadIdx.x + 1024 * j) = v[j];
+    if (pv.splits > 0) *reinterpret_cast<float4*>(xr + col[j]) = v[j];
   }
   ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
   __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kFoldThreads / kWave; ++i) tot += red[i];
   const float r = 1.0f / sqrtf(tot / (float)d + eps);
   T* hr = h + (int64_t)j0 * d;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int c = 4 * threadIdx.x + 1024 * j;
+    if (!ok[j]) continue;
+    const int c = col[j];
     Elt<T>::store(hr, c + 0, (v[j].x * r) * Elt<T>::load(g, c + 0));
     Elt<T>::store(hr, c + 1, (v[j].y * r) * Elt<T>::load(g, c + 1));
     Elt<T>::store(hr, c + 2, (v[j].z * r) * Elt<T>::load(g, c + 2));
@@ -156,22 +170,18 @@ hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R,
 hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
                           float eps, int d, void* h, const PartView& pv, hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (d % 1024 == 0 && d <= 8192) {
-    const int nj = d / 1024;
-#define DLLM_FOLD(TT, NJV)                                                                  \
-  fold_norm_kernel<TT, NJV><<<rows, 256, 0, st>>>(x, Rin, Kout, (const TT*)g, eps, d, (TT*)h, pv)
+  if (d % 4 == 0 && d <= 8192) {
+#define DLLM_FOLD(TT, NJV, GV)                                                    \
+  fold_norm_kernel<TT, NJV, GV><<<rows, kFoldThreads, 0, st>>>(x, Rin, Kout, (const TT*)g, eps, \
+                                                              d, (TT*)h, pv)
     if (dtype == F32) {
-      switch (nj) { case 1: DLLM_FOLD(float, 1); break; case 2: DLLM_FOLD(float, 2); break;
-                    case 4: DLLM_FOLD(float, 4); break; default: goto general; }
+      if (d <= 4096) DLLM_FOLD(float, 1, 16); else DLLM_FOLD(float, 2, 8);
     } else {
-      switch (nj) { case 1: DLLM_FOLD(uint16_t, 1); break; case 2: DLLM_FOLD(uint16_t, 2); break;
-                    case 4: DLLM_FOLD(uint16_t, 4); break; case 8: DLLM_FOLD(uint16_t, 8); break;
-                    default: goto general; }
+      if (d <= 4096) DLLM_FOLD(uint16_t, 1, 16); else DLLM_FOLD(uint16_t, 2, 8);
     }
 #undef DLLM_FOLD
     return hipGetLastError();
   }
-general:
   if (dtype == F32)
     rmsnorm_kernel<float><<<rows, 256, 0, st>>>(x, Rin, Kout, (const float*)g, eps, d, (float*)h, pv);
   else

@@ -92,16 +92,15 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
 
 // ---------------------------------------------------------------- confidence / unmask
 struct ConfPlan {
+  int it = 1;  // 8-element loads per thread per pass (1, 2, 4 or 8)
   int nsplit = 1, chunk = 0;
   size_t part_elems = 0;  // per array (m, s, idx)
-  int counters = 0;
 };
 ConfPlan conf_plan(int rows, int V, int B);
 hipError_t launch_conf_unmask(int ldtype, const ConfPlan& p, const void* logits, int B, int K,
                               int V, int mask_id, float tau, int* tokens, int ld_tokens,
                               float* conf, int* argmax, int* n_unmasked, int* remaining,
-                              int* unmasked_idx, float* pm, float* ps, int* pi, int* counters,
-                              hipStream_t st);
+                              int* unmasked_idx, float* pm, float* ps, int* pi, hipStream_t st);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_rope_table(float* cosb, float* sinb, int S, int D, float theta, hipStream_t st);

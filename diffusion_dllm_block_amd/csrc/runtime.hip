@@ -137,10 +137,10 @@ int step_rows(const Dims& d, int b) {
 }
 
 struct Ws {
-  size_t x, h, q, o, a, logits, rcos, rsin, gpart, gcnt, apart, acnt, cpm, cps, cpi, ccnt,
+  size_t x, h, q, o, a, logits, rcos, rsin, gpart, gcnt, apart, acnt, cpm, cps, cpi,
       conf, argmax, nun, rem, total;
   size_t gpart_floats, apart_floats;
-  int gcnt_n, acnt_n, ccnt_n;
+  int gcnt_n, acnt_n;
 };
 
 void plan_gemms(const Dims& d, int M, bool lm, size_t* pf, int* cn) {
@@ -193,13 +193,11 @@ Ws plan_ws(const Dims& d) {
   // counters last, contiguous, zeroed at prefill
   w.gcnt = take((size_t)gcn * 4);
   w.acnt = take((size_t)acn * 4);
-  w.ccnt = take((size_t)cp.counters * 4);
   w.total = off;
   w.gpart_floats = gpf;
   w.apart_floats = apf;
   w.gcnt_n = gcn;
   w.acnt_n = acn;
-  w.ccnt_n = cp.counters;
   return w;
 }
 
@@ -361,7 +359,7 @@ dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, flo
                              conf ? conf : c.at<float>(c.w.conf),
                              argmax ? argmax : c.at<int>(c.w.argmax), n_un, rem, nullptr,
                              c.at<float>(c.w.cpm), c.at<float>(c.w.cps), c.at<int>(c.w.cpi),
-                             c.at<int>(c.w.ccnt), c.st));
+                             c.st));
   return DLLM_OK;
 }
 
@@ -495,7 +493,7 @@ static size_t kw_attn(int B, int Hq, int R, int S, int D, int dtype, AttnPlan* p
 }
 static size_t kw_conf(int rows, int V, int B, ConfPlan* p) {
   *p = conf_plan(rows, V, B);
-  return up((size_t)p->counters * 4) + 3 * up(p->part_elems * 4);
+  return 3 * up(p->part_elems * 4);
 }
 
 size_t dllm_kernel_workspace_bytes(int32_t B, int32_t Hq, int32_t R, int32_t S, int32_t D,
@@ -551,16 +549,13 @@ dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dty
   if (!ws || ws_bytes < need) return fail(DLLM_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
-  int* cnt = (int*)base;
-  size_t off = up((size_t)p.counters * 4);
-  float* pm = (float*)(base + off);
-  float* ps_ = (float*)(base + off + up(p.part_elems * 4));
-  int* pi = (int*)(base + off + 2 * up(p.part_elems * 4));
-  HIP_TRY(launch_fill_i32(cnt, p.counters, 0, st));
+  float* pm = (float*)base;
+  float* ps_ = (float*)(base + up(p.part_elems * 4));
+  int* pi = (int*)(base + 2 * up(p.part_elems * 4));
   ProfScope ps(DLLM_K_CONF_UNMASK, st);
   HIP_TRY(launch_conf_unmask(logits_dtype, p, logits, B, K, V, mask_id, tau, tokens_block,
                              ld_tokens, conf, argmax, n_unmasked, remaining, unmasked_idx, pm, ps_,
-                             pi, cnt, st));
+                             pi, st));
   return DLLM_OK;
 }
 
