@@ -261,6 +261,9 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the kernel-only rates")
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the kernel-only rates (no generation; for profiling)")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="also run plain device copies of this many MiB (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counter scale)")
     ap.add_argument("--roofline-kernel", default="auto")
     ap.add_argument("--logit-scale", type=float, default=0.0,
                     help="override the calibrated scale (exploration only)")
@@ -275,6 +278,16 @@ def main():
     from diffusion_dllm_block_amd.engine import Model, Session
 
     lib = bd.load()
+    if a.copy_probe_mb:
+        # one elementwise kernel per call that reads and writes exactly n bytes each
+        n = a.copy_probe_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: 4 elementwise copies of {n} bytes")
+        del src, dst
     if a.kernels_only:
         print(json.dumps({"kernels": kernel_only(lib, torch, bd)}), flush=True)
         return

@@ -304,21 +304,23 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
     arow[i] = X + (int64_t)m * ldx + kb + 8 * c8;
     brow[i] = W + (int64_t)wrow_of<EPI>(vc, e.F) * K + kb + 8 * c8;
   }
-  u32x4 ra[4], rb[4];
-  auto load = [&](int st) {
+  // two register sets: the global loads of stage s + 2 are issued before stage s is
+  // computed, so they have two compute phases to arrive
+  u32x4 ra[2][4], rb[2][4];
+  auto load = [&](int set, int st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(arow[i] + st * TB_K);
-      rb[i] = *reinterpret_cast<const u32x4*>(brow[i] + st * TB_K);
+      ra[set][i] = *reinterpret_cast<const u32x4*>(arow[i] + st * TB_K);
+      rb[set][i] = *reinterpret_cast<const u32x4*>(brow[i] + st * TB_K);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int set, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       int ee = tid + 256 * i;
       int r = ee >> 3, c8 = ee & 7;
-      *reinterpret_cast<u32x4*>(&As[(buf * 128 + r) * TB_LD + 8 * c8]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[(buf * 128 + r) * TB_LD + 8 * c8]) = rb[i];
+      *reinterpret_cast<u32x4*>(&As[(buf * 128 + r) * TB_LD + 8 * c8]) = ra[set][i];
+      *reinterpret_cast<u32x4*>(&Bs[(buf * 128 + r) * TB_LD + 8 * c8]) = rb[set][i];
     }
   };
   f32x16 acc[2][2];
@@ -343,14 +345,26 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
     }
   };
 
-  load(0);
-  store(0);
+  // stage s lives in LDS buffer s & 1 and register set s & 1
+  load(0, 0);
+  store(0, 0);
+  if (nst > 1) load(1, 1);
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) load(st + 1);
-    compute(st & 1);
-    if (st + 1 < nst) store((st + 1) & 1);
+  // pairs of stages (one loop latch: the accumulators keep their registers)
+  int st = 0;
+  for (; st + 1 < nst; st += 2) {
+    if (st + 2 < nst) load(0, st + 2);
+    compute(0);
+    store(1, 1);
     __syncthreads();
+    if (st + 3 < nst) load(1, st + 3);
+    compute(1);
+    if (st + 2 < nst) store(0, 0);
+    __syncthreads();
+  }
+  if (st < nst) {  // odd stage count: the last stage is in buffer 0
+    compute(0);
+    __syncthreads();  // the epilogue tile below reuses the operand buffers
   }
 
 #pragma unroll
@@ -383,6 +397,135 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
   gather_partials(tile, TL, 128, m0, vc0, M, Nv, splits, part);
   __syncthreads();
   epilogue<uint16_t, EPI>(tile, TL, 128, m0, vc0, M, Nv, e);
+}
+
+// ============================================================================
+// large bf16 GEMM (M >= 512, the refresh): 256x256 output tiles, 8 waves (two per
+// SIMD, so one can issue MFMAs while the other waits) each computing 128 rows x 64
+// columns with 32x32x16 MFMAs; 64-wide K stages double-buffered in LDS, the global
+// loads of stage s + 1 in flight while stage s is computed, and the LDS operands of
+// step kk + 1 read while step kk is in the MFMAs.  The epilogue runs one 128x128
+// quarter at a time through an fp32 LDS tile (the 128-column virtual tiles of the
+// other kernels).  Residual GEMMs with too few tiles split K and leave fp32 partials
+// [split][M][Nv] for the next RMSNorm.
+// ============================================================================
+constexpr int BG_T = 256;                                   // output tile (rows = cols)
+constexpr int BG_THREADS = 512;
+constexpr int BG_AB_BYTES = 2 * 2 * BG_T * TB_LD * 2;       // A and B, double-buffered
+constexpr int BG_TILE_BYTES = 128 * TL * 4;                 // one 128x128 quarter, fp32
+constexpr int BG_SMEM = BG_AB_BYTES > BG_TILE_BYTES ? BG_AB_BYTES : BG_TILE_BYTES;
+
+template <int EPI>
+__global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
+    const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv, int K,
+    int kchunk, int splits, float* part, EpiArgs e) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char bg_smem[];
+  uint16_t* As = reinterpret_cast<uint16_t*>(bg_smem);
+  uint16_t* Bs = As + 2 * BG_T * TB_LD;
+  float* tile = reinterpret_cast<float*>(bg_smem);
+  const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+  const int m0 = tm * BG_T, vc0 = tn * BG_T;
+  const int tid = threadIdx.x;
+  // wave w: rows 128 (w & 1) .. +128, columns 64 (w >> 1) .. +64
+  const int w = tid >> 6, wm = w & 1, wn = w >> 1, l = tid & 63, lr = l & 31, g = l >> 5;
+  const int kb = split * kchunk;
+  const int ke = min(K, kb + kchunk);
+  const int nst = (ke - kb) / TB_K;
+
+  // loader: element e = tid + 512 i (i < 4) -> tile row e >> 3, 16-byte column e & 7;
+  // rows past M / columns past Nv load a clamped valid row (results discarded)
+  const int lrow = tid >> 3, lc8 = tid & 7;
+  const uint16_t* abase[4];
+  const uint16_t* bbase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = lrow + 64 * i;
+    abase[i] = X + (int64_t)min(m0 + r, M - 1) * ldx + kb + 8 * lc8;
+    bbase[i] = W + (int64_t)wrow_of<EPI>(min(vc0 + r, Nv - 1), e.F) * K + kb + 8 * lc8;
+  }
+  u32x4 ra[4], rb[4];
+  auto load = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = *reinterpret_cast<const u32x4*>(abase[i] + st * TB_K);
+      rb[i] = *reinterpret_cast<const u32x4*>(bbase[i] + st * TB_K);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = lrow + 64 * i;
+      *reinterpret_cast<u32x4*>(&As[(buf * BG_T + r) * TB_LD + 8 * lc8]) = ra[i];
+      *reinterpret_cast<u32x4*>(&Bs[(buf * BG_T + r) * TB_LD + 8 * lc8]) = rb[i];
+    }
+  };
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  auto frag = [&](int buf, int kk, u32x4* a, u32x4* b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const u32x4*>(
+          &As[(buf * BG_T + wm * 128 + i * 32 + lr) * TB_LD + 16 * kk + 8 * g]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b[j] = *reinterpret_cast<const u32x4*>(
+          &Bs[(buf * BG_T + wn * 64 + j * 32 + lr) * TB_LD + 16 * kk + 8 * g]);
+  };
+  auto compute = [&](int buf) {
+    u32x4 a[2][4], b[2][2];
+    frag(buf, 0, a[0], b[0]);
+#pragma unroll
+    for (int kk = 0; kk < TB_K / 16; ++kk) {
+      if (kk + 1 < TB_K / 16) frag(buf, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = mfma32(as_bf16x8(a[kk & 1][i]), as_bf16x8(b[kk & 1][j]), acc[i][j]);
+    }
+  };
+
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) load(st + 1);
+    compute(buf);
+    if (st + 1 < nst) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue, one 128x128 quarter (two waves) at a time
+  for (int p = 0; p < 4; ++p) {
+    const int qm = p >> 1, qn = p & 1;  // quarter rows 128 qm, columns 128 qn
+    if (wm == qm && (wn >> 1) == qn) {
+      const int c0 = (wn & 1) * 64;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            tile[(i * 32 + acc_row(v, g)) * TL + c0 + j * 32 + lr] = acc[i][j][v];
+    }
+    __syncthreads();
+    const int pm0 = m0 + 128 * qm, pvc0 = vc0 + 128 * qn;
+    if (splits == 1) {
+      epilogue<uint16_t, EPI>(tile, TL, 128, pm0, pvc0, M, Nv, e);
+    } else {
+      // residual GEMM split over K: partials summed by the next RMSNorm in split order
+      for (int i = tid; i < 128 * 128; i += BG_THREADS) {
+        const int r = i >> 7, c = i & 127;
+        const int m = pm0 + r, vc = pvc0 + c;
+        if (m < M && vc < Nv) part[((int64_t)split * M + m) * Nv + vc] = tile[r * TL + c];
+      }
+    }
+    __syncthreads();
+  }
 }
 
 // ============================================================================
@@ -560,6 +703,35 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     p.deferred = true;  // partials reduced by the next RMSNorm or by reduce_epilogue
     return p;
   }
+  // large GEMMs: 256x256 tiles unless their count fills the chip much worse than the
+  // 128x128 tiles' (the large tile does ~15% more work per unit time)
+  auto fill = [](int tiles, int slots) {
+    const int waves = (tiles + slots - 1) / slots;
+    return (double)tiles / ((double)waves * slots);
+  };
+  const int big_tiles = ((Nv + BG_T - 1) / BG_T) * ((M + BG_T - 1) / BG_T);
+  const int small_tiles = ((Nv + 127) / 128) * ((M + 127) / 128);
+  const bool big_fills = (epi == EPI_RESID && big_tiles < 256) ||
+                         1.15 * fill(big_tiles, 256) >= fill(small_tiles, 512);
+  if (M >= 512 && K % TB_K == 0 && big_fills) {
+    p.kind = GEMM_BIG;
+    p.ntn = (Nv + BG_T - 1) / BG_T;
+    p.ntm = (M + BG_T - 1) / BG_T;
+    const int tiles = p.ntn * p.ntm;
+    int splits = 1;
+    if (epi == EPI_RESID && tiles < 256) {  // fill the chip: split K, deferred partials
+      splits = (256 + tiles - 1) / tiles;
+      if (splits > K / TB_K) splits = K / TB_K;
+    }
+    const int per = (K + splits - 1) / splits;
+    p.kchunk = (per + TB_K - 1) / TB_K * TB_K;
+    p.splits = (K + p.kchunk - 1) / p.kchunk;
+    if (p.splits > 1) {
+      p.part_floats = (size_t)p.splits * M * Nv;
+      p.deferred = true;
+    }
+    return p;
+  }
   p.kind = GEMM_TILED;
   p.ntn = (Nv + 127) / 128;
   p.ntm = (M + 127) / 128;
@@ -635,6 +807,16 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
       else DLLM_SKINNY(4, 256);
     }
 #undef DLLM_SKINNY
+  } else if (p.kind == GEMM_BIG) {
+    static bool attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
+    if (!attr_set) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_bf16<EPI>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, BG_SMEM);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+    gemm_big_bf16<EPI><<<dim3(p.ntn, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
+        (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e);
   } else {
     gemm_tiled_bf16<EPI><<<dim3(p.ntn, p.ntm, p.splits), 256, 0, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, counters,

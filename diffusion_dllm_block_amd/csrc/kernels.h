@@ -33,7 +33,7 @@ struct EpiArgs {
   int Hq = 0, Hkv = 0, D = 0, R = 0, pos0 = 0, Sp = 0;
 };
 
-enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2 };
+enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3 };
 
 // Where split-K partial sums live.  Plain: [split][M][N].  Blocked (skinny GEMM): per split,
 // per 16-column group, one block of mrows x 16 floats in which row m, column c sits at

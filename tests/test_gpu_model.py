@@ -112,10 +112,12 @@ def small_bf16(Hq=2, Hkv=2, mode="dual", B=2, P=40, G=64, K=32, V=2048, gain=0.1
                           cache_mode=mode, norm_gain_std=gain)
 
 
-@pytest.mark.parametrize("Hq,Hkv,mode,B,K", [(2, 2, "dual", 2, 32), (4, 1, "dual", 3, 16),
-                                           (2, 2, "prefix", 2, 32), (2, 1, "prefix", 1, 8)])
-def test_small_bf16_teacher_forced(lib, Hq, Hkv, mode, B, K):
-    wl = small_bf16(Hq, Hkv, mode, B=B, K=K)
+@pytest.mark.parametrize("Hq,Hkv,mode,B,K,P", [(2, 2, "dual", 2, 32, 40), (4, 1, "dual", 3, 16, 40),
+                                             (2, 2, "prefix", 2, 32, 40), (2, 1, "prefix", 1, 8, 40),
+                                             (2, 1, "dual", 2, 32, 400)])
+def test_small_bf16_teacher_forced(lib, Hq, Hkv, mode, B, K, P):
+    # P = 400: B * S = 928 rows, so the refresh runs the large-tile GEMM path
+    wl = small_bf16(Hq, Hkv, mode, B=B, K=K, P=P)
     worst, checked, excluded = teacher_forced(lib, wl, 2e-2, False)
     # bf16 logits differ by ~5e-3 relative, which moves confidences by up to
     # conf * (exp(2 dl) - 1): most decisions are inside that band, so end-to-end bf16
