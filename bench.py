@@ -44,6 +44,12 @@ DOMINANT = {
 }
 
 
+METRIC = {
+    "llada8b_dual_p1000_g1024":
+        "generated tokens/sec @1 GPU (LLaDA-8B-shape, DualCache, \u03c4=0.9); attn GB/s",
+}
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -350,7 +356,7 @@ def main():
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
 
     out = {
-        "metric": "generated tokens/sec @1 GPU (LLaDA-8B-shape, DualCache, tau=0.9)",
+        "metric": METRIC.get(wl.name, f"generated tokens/sec @1 GPU ({wl.name})"),
         "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(dt / a.steps * 1e3, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",

@@ -127,16 +127,6 @@ __device__ __forceinline__ void gather_partials(float* tile, int ldt, int rows, 
 // ============================================================================
 // skinny bf16 GEMM (M <= 64): weight streaming
 // ============================================================================
-// Workgroup = 8 waves over a tile of 64 virtual columns and a K range of 1024 (512 when
-// M > 32): wave w owns columns 16*(w&3)..+16 and the (w>>2)-th half of the K range.
-// The activation slice X[M][K range] is loaded once into LDS; each wave issues all of
-// its weight loads (16 x 16 bytes per lane, straight into 16x16x32 MFMA operand
-// registers) before its first MFMA, so there is no per-stage barrier and the whole
-// slice of W is in flight at once.  The two K halves are summed in LDS; K ranges are
-// combined across workgroups as described for the split-K schemes above.
-constexpr int S2_NT = 64;          // virtual columns per workgroup
-constexpr int S2_TL = S2_NT + 4;   // LDS row stride of the fp32 result tile
-
 // virtual column -> weight row for 64-column tiles:
 //   SWIGLU: tile t = gate rows 32t..+32 then up rows F+32t..+32;
 //   QKV (head_dim 128): tile t = head t/2, dims 32(t&1)..+32 then the same dims + 64,
@@ -154,70 +144,72 @@ __device__ __forceinline__ int wrow_s2(int vc, int F) {
   }
 }
 
-// Workgroup = 8 independent waves pinned to one K range of KR.  Each wave computes 16
-// virtual columns over the whole K range (NLOAD = KR/32 weight loads of 16 bytes per lane
-// in flight).  XV = 16-byte activation loads per thread to fill the LDS slice.
-template <int MT, int KR> struct SkinnyCfg {
-  static constexpr int NLOAD = KR / 32;
-  static constexpr int LDX = KR + 8;                 // LDS row stride (elements)
-  static constexpr int XV = MT * 16 * KR / 8 / 512;
+// Persistent weight-streaming GEMM for M <= 64 rows.
+//   * One 8-wave workgroup per CU, pinned to one K range of KW = 8 * KS
+//     (blockIdx % splits); its activation slice X[M][KW] is loaded into LDS once.
+//   * The workgroup walks 16-column groups (wid, wid + nw, ...).  For a group, wave w
+//     covers the K sub-range [w KS, (w+1) KS) with 16x16x32 MFMAs; the 8 partial sums
+//     are added in LDS in wave order, and each of the MT*4 result rows of 64 lanes is
+//     written as one 256-byte store (blocked partial layout, PartView in kernels.h).  So
+//     a wave keeps only KS/32 loads per lane in flight (a modest, steady stream per CU)
+//     while the partials written per group are those of one K range of KW.
+//   * Register t is refilled with the next group's weights right after the MFMAs of
+//     step t consumed it.  After the last group the refills read one fixed cached line
+//     instead of branching: no data-dependent branches, so the wait counts stay exact.
+//   * Partials (virtual column order) are summed in split order by reduce_epilogue, or
+//     for the residual GEMMs by the next RMSNorm.
+template <int MT, int KS> struct SkinnyCfg {
+  static constexpr int KW = 8 * KS;                  // K range of a workgroup
+  static constexpr int NLOAD = KS / 32;              // weight loads per lane per group
+  static constexpr int LDX = KW + 8;                 // LDS row stride (elements)
+  static constexpr int XV = MT * 16 * KW / 8 / 512;  // 16-byte activation loads per thread
+  static constexpr int SLOTS = MT * 4;               // result rows of 64 lanes per group
   static_assert(XV >= 1, "activation slice smaller than one load per thread");
+  static_assert(MT * 16 * LDX * 2 + 8 * SLOTS * 64 * 4 <= 160 * 1024, "LDS budget");
 };
 
-// Persistent weight-streaming GEMM for M <= 64 rows.
-//   * One workgroup per CU, pinned to one K range (blockIdx % splits); its activation
-//     slice X[M][KR] is loaded into LDS once.
-//   * Its 8 waves walk 16-column groups independently (group = wid*8 + wave, then + nw*8):
-//     no barrier after the slice is loaded.
-//   * Each lane keeps NLOAD weight loads in flight: register t is refilled with the next
-//     group's weights right after the MFMAs of step t consumed it, so the weight stream
-//     does not pause between groups.  After the last group the refills read one fixed
-//     cached line instead of branching, and every group writes its whole padded block
-//     of partials: no data-dependent branches, so the compiler's wait counts stay exact.
-//   * Partials (blocked layout, virtual column order) are summed in split order by
-//     reduce_epilogue, or for the residual GEMMs by the next RMSNorm.
-template <int MAP, int MT, int KR>
+template <int MAP, int MT, int KS>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_skinny_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv,
     int K, int F, int splits, int ngrp, float* __restrict__ part) {
-  using C = SkinnyCfg<MT, KR>;
+  using C = SkinnyCfg<MT, KS>;
   __shared__ __attribute__((aligned(16))) uint16_t Xs[MT * 16 * C::LDX];
+  __shared__ __attribute__((aligned(16))) float red[8][C::SLOTS][64];
   const int split = blockIdx.x % splits;
   const int wid = blockIdx.x / splits;
   const int nw = gridDim.x / splits;  // workgroups per K range (grid is a multiple of splits)
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, ln = l & 15, g = l >> 4;
-  const int kb = split * KR;
+  const int kw0 = split * C::KW;      // the workgroup's K range
+  const int ks0 = kw0 + w * KS;       // this wave's K sub-range
 
   {  // activation slice -> LDS (rows >= M read row M-1; their outputs are never used)
     u32x4 xr[C::XV];
 #pragma unroll
     for (int i = 0; i < C::XV; ++i) {
       const int ee = tid + 512 * i;
-      const int r = ee / (KR / 8), c8 = ee % (KR / 8);
-      xr[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(r, M - 1) * ldx + kb + 8 * c8);
+      const int r = ee / (C::KW / 8), c8 = ee % (C::KW / 8);
+      xr[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(r, M - 1) * ldx + kw0 + 8 * c8);
     }
 #pragma unroll
     for (int i = 0; i < C::XV; ++i) {
       const int ee = tid + 512 * i;
-      const int r = ee / (KR / 8), c8 = ee % (KR / 8);
+      const int r = ee / (C::KW / 8), c8 = ee % (C::KW / 8);
       *reinterpret_cast<u32x4*>(&Xs[r * C::LDX + 8 * c8]) = xr[i];
     }
   }
   __syncthreads();
-  const int grp0 = wid * 8 + w;
-  if (grp0 >= ngrp) return;  // no barrier follows
+  if (wid >= ngrp) return;  // uniform over the workgroup; no barrier follows for it
 
   auto wptr = [&](int grp) {  // columns past Nv read a clamped valid row (never used)
     const int vc = min(grp * 16 + ln, Nv - 1);
-    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + kb + 8 * g;
+    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + ks0 + 8 * g;
   };
   u32x4 wr[C::NLOAD];
   {
     // issued in t order, like the refills in the loop, so that the loop's wait counts
-    // are the same on entry and on the back edge (otherwise the compiler falls back to
-    // waiting for every load at the top of each group)
-    const uint16_t* wp = wptr(grp0);
+    // are the same on entry and on the back edge
+    const uint16_t* wp = wptr(wid);
 #pragma unroll
     for (int t = 0; t < C::NLOAD; ++t) {
       wr[t] = *reinterpret_cast<const u32x4*>(wp + 32 * t);
@@ -225,42 +217,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
-  for (int grp = grp0; grp < ngrp; grp += nw * 8) {
-    const bool has_next = grp + nw * 8 < ngrp;
-    // refill source: the next group, or (after the last group) the first KR elements of
-    // W, which stay cached; the same offsets keep the loads' addresses immediate
-    const uint16_t* wpn = has_next ? wptr(grp + nw * 8) : W + 8 * g;
+  const uint16_t* xs = &Xs[ln * C::LDX + w * KS + 8 * g];
+  for (int grp = wid; grp < ngrp; grp += nw) {
+    const bool has_next = grp + nw < ngrp;
+    // refill source: the next group, or (after the last group) this wave's first weight
+    // line, which stays cached; the same offsets keep the loads' addresses immediate
+    const uint16_t* wpn = has_next ? wptr(grp + nw) : W + ks0 + 8 * g;
     f32x4 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{};
-    // activation operands are read one step ahead; the scheduling barrier keeps the
-    // compiler from hoisting every LDS read (which would need ~2*NLOAD*MT registers)
-    const uint16_t* xs = &Xs[ln * C::LDX + 8 * g];
-    u32x4 a_cur[MT], a_nxt[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      a_cur[mt] = *reinterpret_cast<const u32x4*>(xs + mt * 16 * C::LDX);
 #pragma unroll
     for (int t = 0; t < C::NLOAD; ++t) {
-      if (t + 1 < C::NLOAD) {
+      u32x4 a[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          a_nxt[mt] = *reinterpret_cast<const u32x4*>(xs + mt * 16 * C::LDX + 32 * (t + 1));
-      }
+      for (int mt = 0; mt < MT; ++mt)
+        a[mt] = *reinterpret_cast<const u32x4*>(xs + mt * 16 * C::LDX + 32 * t);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(as_bf16x8(a_cur[mt]), as_bf16x8(wr[t]), acc[mt]);
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = mfma16(as_bf16x8(a[mt]), as_bf16x8(wr[t]), acc[mt]);
       wr[t] = *reinterpret_cast<const u32x4*>(wpn + 32 * t);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) a_cur[mt] = a_nxt[mt];
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane (column ln, group g) holds rows mt*16 + 4g + r: blocked partial layout, one
-    // 256-byte contiguous store per (mt, r) (PartView in kernels.h)
-    float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
+    // lane (column ln, group g) holds rows mt*16 + 4g + r: slot mt*4 + r
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) blk[(mt * 4 + r) * 64 + l] = acc[mt][r];
+      for (int r = 0; r < 4; ++r) red[w][mt * 4 + r][l] = acc[mt][r];
+    __syncthreads();
+    float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
+    for (int sl = w; sl < C::SLOTS; sl += 8) {
+      float v = red[0][sl][l];
+#pragma unroll
+      for (int ww = 1; ww < 8; ++ww) v += red[ww][sl][l];
+      blk[sl * 64 + l] = v;
+    }
+    __syncthreads();  // red is rewritten by the next group
   }
 }
 
@@ -690,15 +680,16 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   if (M <= 64) {
     p.kind = GEMM_SKINNY;
     p.mt = (M <= 16) ? 1 : (M <= 32) ? 2 : 4;
-    p.ntn = (Nv + S2_NT - 1) / S2_NT;
+    p.ntn = (Nv + 15) / 16;  // 16-column groups
     p.ntm = 1;
-    // K range per workgroup: the largest of 1024/512/256 dividing K whose activation
-    // slice fits the LDS budget (M > 32 rows: at most 512)
-    int kr = 256;
-    if (K % 1024 == 0 && p.mt <= 2) kr = 1024;
-    else if (K % 512 == 0) kr = 512;
-    p.kchunk = kr;
-    p.splits = K / kr;
+    // per-wave K sub-range KS (the workgroup covers 8 KS): the largest of 256/128/64/32
+    // with K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 64)
+    int ks = 32;
+    for (int c : {256, 128, 64}) {
+      if (K % (8 * c) == 0 && (p.mt <= 2 || c <= 64)) { ks = c; break; }
+    }
+    p.kchunk = 8 * ks;
+    p.splits = K / p.kchunk;
     p.part_floats = (size_t)p.splits * ((Nv + 15) / 16) * (p.mt * 16 * 16);  // blocked layout
     p.deferred = true;  // partials reduced by the next RMSNorm or by reduce_epilogue
     return p;
@@ -786,25 +777,28 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
     const int ngrp = (Nv + 15) / 16;
     int per_split = num_cus() / p.splits;
     if (per_split < 1) per_split = 1;
-    if (per_split > (ngrp + 7) / 8) per_split = (ngrp + 7) / 8;
+    if (per_split > ngrp) per_split = ngrp;
     dim3 grid(per_split * p.splits);
     const uint16_t* Xb = (const uint16_t*)X;
     const uint16_t* Wb = (const uint16_t*)W;
     constexpr int MAP = (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? EPI : EPI_STORE;
-#define DLLM_SKINNY(MTV, KRV)                                                           \
-    gemm_skinny_bf16<MAP, MTV, KRV><<<grid, 512, 0, st>>>(Xb, ldx, Wb, M, Nv, K, e.F,  \
+#define DLLM_SKINNY(MTV, KSV)                                                           \
+    gemm_skinny_bf16<MAP, MTV, KSV><<<grid, 512, 0, st>>>(Xb, ldx, Wb, M, Nv, K, e.F,  \
                                                          p.splits, ngrp, part)
+    const int ks = p.kchunk / 8;
     if (p.mt == 1) {
-      if (p.kchunk == 1024) DLLM_SKINNY(1, 1024);
-      else if (p.kchunk == 512) DLLM_SKINNY(1, 512);
-      else DLLM_SKINNY(1, 256);
+      if (ks == 256) DLLM_SKINNY(1, 256);
+      else if (ks == 128) DLLM_SKINNY(1, 128);
+      else if (ks == 64) DLLM_SKINNY(1, 64);
+      else DLLM_SKINNY(1, 32);
     } else if (p.mt == 2) {
-      if (p.kchunk == 1024) DLLM_SKINNY(2, 1024);
-      else if (p.kchunk == 512) DLLM_SKINNY(2, 512);
-      else DLLM_SKINNY(2, 256);
+      if (ks == 256) DLLM_SKINNY(2, 256);
+      else if (ks == 128) DLLM_SKINNY(2, 128);
+      else if (ks == 64) DLLM_SKINNY(2, 64);
+      else DLLM_SKINNY(2, 32);
     } else {
-      if (p.kchunk == 512) DLLM_SKINNY(4, 512);
-      else DLLM_SKINNY(4, 256);
+      if (ks == 64) DLLM_SKINNY(4, 64);
+      else DLLM_SKINNY(4, 32);
     }
 #undef DLLM_SKINNY
   } else if (p.kind == GEMM_BIG) {

@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_norm_kernel(float* x, int R
   const int64_t stride = pv.split_stride();
   const int tid = threadIdx.x;
   float4 v[NJ];
+  float gv[NJ][4];  // the gains, read together with x and the partials
   bool ok[NJ];
   int col[NJ];
 #pragma unroll
@@ -89,6 +90,8 @@ __global__ __launch_bounds__(kFoldThreads) void fold_norm_kernel(float* x, int R
     ok[j] = col[j] < d;
     col[j] = ok[j] ? col[j] : 0;  // clamped, never stored
     v[j] = *reinterpret_cast<const float4*>(xr + col[j]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gv[j][u] = Elt<T>::load(g, col[j] + u);
   }
   for (int s0 = 0; s0 < pv.splits; s0 += G) {
     float4 pvv[G][NJ];
@@ -126,10 +129,13 @@ __global__ __launch_bounds__(kFoldThreads) void fold_norm_kernel(float* x, int R
   for (int j = 0; j < NJ; ++j) {
     if (!ok[j]) continue;
     const int c = col[j];
-    Elt<T>::store(hr, c + 0, (v[j].x * r) * Elt<T>::load(g, c + 0));
-    Elt<T>::store(hr, c + 1, (v[j].y * r) * Elt<T>::load(g, c + 1));
-    Elt<T>::store(hr, c + 2, (v[j].z * r) * Elt<T>::load(g, c + 2));
-    Elt<T>::store(hr, c + 3, (v[j].w * r) * Elt<T>::load(g, c + 3));
+    const float o0 = (v[j].x * r) * gv[j][0], o1 = (v[j].y * r) * gv[j][1];
+    const float o2 = (v[j].z * r) * gv[j][2], o3 = (v[j].w * r) * gv[j][3];
+    if constexpr (sizeof(T) == 2) {  // bf16: one 8-byte store
+      *reinterpret_cast<u16x4*>(hr + c) = u16x4{f2bf(o0), f2bf(o1), f2bf(o2), f2bf(o3)};
+    } else {
+      *reinterpret_cast<float4*>(hr + c) = make_float4(o0, o1, o2, o3);
+    }
   }
 }
 
