@@ -104,11 +104,18 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
     Hkv = k.shape[1]
     group = Hq // Hkv
     o = np.empty_like(q)
-    for h in range(Hq):
-        kv = h // group
-        s = np.matmul(q[:, h], np.swapaxes(k[:, kv], -1, -2)) / np.sqrt(D)
-        o[:, h] = np.matmul(softmax(s, -1), v[:, kv])
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // group
+            s = (q[b, h] @ k[b, kv].T) / np.sqrt(D)                # [R, S]
+            o[b, h] = softmax(s, -1) @ v[b, kv]
     return o
+
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """x [..., K] . w[N, K]^T as one 2-D product (so the library GEMM is used)."""
+    y = x.reshape(-1, x.shape[-1]) @ w.T
+    return y.reshape(x.shape[:-1] + (w.shape[0],))
 
 
 def silu(x: np.ndarray) -> np.ndarray:
@@ -174,11 +181,14 @@ def layer_qkv(M: OracleModel, l: int, x: np.ndarray, positions: np.ndarray):
     B, R, _ = x.shape
     D, Hq, Hkv = m.head_dim, m.n_heads, m.n_kv_heads
     h = M.rs(rmsnorm(x, M.w("attn_norm", l), m.norm_eps))
-    qkv = np.matmul(h, M.w("w_qkv", l).T)                       # [B,R,(Hq+2Hkv)D]
+    qkv = linear(h, M.w("w_qkv", l))                             # [B,R,(Hq+2Hkv)D]
     q = qkv[..., :Hq * D].reshape(B, R, Hq, D).transpose(0, 2, 1, 3)
     k = qkv[..., Hq * D:(Hq + Hkv) * D].reshape(B, R, Hkv, D).transpose(0, 2, 1, 3)
     v = qkv[..., (Hq + Hkv) * D:].reshape(B, R, Hkv, D).transpose(0, 2, 1, 3)
     cos, sin = rope_cos_sin(positions, D, m.rope_theta)
+    # tables in the compute dtype: a float32 oracle stays in float32 (the tables are
+    # then the fp32 values a float32 implementation stores); float64 is unchanged
+    cos, sin = cos.astype(M.dtype), sin.astype(M.dtype)
     q = M.rs(apply_rope(q, cos, sin))
     k = M.rs(apply_rope(k, cos, sin))
     v = M.rs(v)
@@ -192,11 +202,11 @@ def layer_rest(M: OracleModel, l: int, x: np.ndarray, q: np.ndarray, K: np.ndarr
     B, R, d = x.shape
     o = M.rs(attention(q, K, V))                                 # [B,Hq,R,D]
     o = o.transpose(0, 2, 1, 3).reshape(B, R, m.n_heads * m.head_dim)
-    x = M.rf(x + np.matmul(o, M.w("w_o", l).T))
+    x = M.rf(x + linear(o, M.w("w_o", l)))
     h = M.rs(rmsnorm(x, M.w("ffn_norm", l), m.norm_eps))
-    gu = np.matmul(h, M.w("w_gate_up", l).T)
+    gu = linear(h, M.w("w_gate_up", l))
     a = M.rs(silu(gu[..., :m.d_ffn]) * gu[..., m.d_ffn:])
-    return M.rf(x + np.matmul(a, M.w("w_down", l).T))
+    return M.rf(x + linear(a, M.w("w_down", l)))
 
 
 def embed(M: OracleModel, tokens: np.ndarray) -> np.ndarray:
@@ -207,7 +217,7 @@ def lm_head(M: OracleModel, x: np.ndarray) -> np.ndarray:
     """Final RMSNorm, LM head, logit scale.  x [B,R,d] -> logits [B,R,V]."""
     m = M.m
     h = M.rs(rmsnorm(x, M.w("final_norm"), m.norm_eps))
-    return M.rf(m.logit_scale * np.matmul(h, M.w("lm_head").T))
+    return M.rf(m.logit_scale * linear(h, M.w("lm_head")))
 
 
 # ----------------------------------------------------------------------------------
