@@ -94,7 +94,10 @@ __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
   }
 }
 
-__global__ __launch_bounds__(256) void attn_splitkv_bf16(
+// ONE: every wave has a single 32-key sub-tile (nsub == 1): one operand tile in
+// registers, so two workgroups fit on a CU.
+template <bool ONE>
+__global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
     int Sp, int nqt, int nchunk, int nsub, float scale_log2, float* __restrict__ part_o,
@@ -176,14 +179,20 @@ __global__ __launch_bounds__(256) void attn_splitkv_bf16(
     }
   };
 
-  KVTile16 ta, tb;
-  load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
-  for (int n = 0; n < nsub; n += 2) {
-    if (n + 1 < nsub) load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
-    consume(ta, wkey0 + 32 * n);
-    if (n + 1 >= nsub) break;
-    if (n + 2 < nsub) load_kv16(ta, kbase, vbase, wkey0 + 32 * (n + 2), li, j, S, Sp);
-    consume(tb, wkey0 + 32 * (n + 1));
+  if constexpr (ONE) {
+    KVTile16 ta;
+    load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
+    consume(ta, wkey0);
+  } else {
+    KVTile16 ta, tb;
+    load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
+    for (int n = 0; n < nsub; n += 2) {
+      if (n + 1 < nsub) load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
+      consume(ta, wkey0 + 32 * n);
+      if (n + 1 >= nsub) break;
+      if (n + 2 < nsub) load_kv16(ta, kbase, vbase, wkey0 + 32 * (n + 2), li, j, S, Sp);
+      consume(tb, wkey0 + 32 * (n + 1));
+    }
   }
 
   // ---- merge the 4 waves (fixed order)
@@ -247,56 +256,53 @@ __global__ __launch_bounds__(256) void attn_splitkv_bf16(
 }
 
 // Merge the chunk partials: o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, chunks in
-// order.  grid (B*Hq*nqt, 4): workgroup y handles 8 query rows of the 32-row tile.
+// order.  grid (B*Hq*nqt, 8), 128 threads: workgroup y handles query rows 4y .. 4y+3 of
+// the 32-row tile, thread -> (row, 4 dims).  Every thread computes its row's weights
+// itself (the (m, l) pairs are 2 * nchunk broadcast loads), and the partial loads of up
+// to 16 chunks are issued together.
 constexpr int kMaxChunks = 64;
-__global__ __launch_bounds__(256) void attn_combine(const float* __restrict__ part_o,
+constexpr int kCombRows = 4;
+__global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ part_o,
                                                     const float* __restrict__ part_ml,
                                                     uint16_t* __restrict__ o, int Hq, int R,
                                                     int nqt, int nchunk) {
-  __shared__ float wts[kMaxChunks][8];
   const int64_t grp = blockIdx.x;
   const int qt = (int)(grp % nqt);
   const int hq = (int)((grp / nqt) % Hq);
   const int b = (int)(grp / ((int64_t)nqt * Hq));
-  const int q0 = blockIdx.y * 8;
+  const int qi = blockIdx.y * kCombRows + (threadIdx.x >> 5), d4 = (threadIdx.x & 31) * 4;
+  const int row = qt * 32 + qi;
   const float* pml = part_ml + grp * nchunk * 64;
-  if (threadIdx.x < 8) {
-    const int qi = q0 + threadIdx.x;
-    float M = -INFINITY;
-    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, pml[c * 64 + qi]);
-    float L = 0.f;
-    for (int c = 0; c < nchunk; ++c) {
-      float mc = pml[c * 64 + qi];
-      float f = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
-      wts[c][threadIdx.x] = f;
-      L += pml[c * 64 + 32 + qi] * f;
-    }
-    const float inv = 1.0f / L;
-    for (int c = 0; c < nchunk; ++c) wts[c][threadIdx.x] *= inv;
-  }
-  __syncthreads();
-  // thread -> (query q0 + tid/32, dims 4*(tid%32) .. +4)
-  const int qi = threadIdx.x >> 5, d4 = (threadIdx.x & 31) * 4;
-  const int row = qt * 32 + q0 + qi;
-  const float* pb = part_o + grp * nchunk * (32 * HD) + (q0 + qi) * HD + d4;
+  const float* pb = part_o + grp * nchunk * (32 * HD) + qi * HD + d4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < nchunk; c0 += 8) {
-    float4 v[8];
+  float M = -INFINITY, L = 0.f;
+  for (int c0 = 0; c0 < nchunk; c0 += 16) {
+    float mc[16], lc[16];
+    float4 v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      v[u] = (c0 + u < nchunk) ? *reinterpret_cast<const float4*>(pb + (int64_t)(c0 + u) * 32 * HD)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < 16; ++u) {
+      const int c = min(c0 + u, nchunk - 1);  // clamped; chunks past nchunk are dropped
+      mc[u] = pml[c * 64 + qi];
+      lc[u] = pml[c * 64 + 32 + qi];
+      v[u] = *reinterpret_cast<const float4*>(pb + (int64_t)c * 32 * HD);
+    }
+    // online merge in chunk order (the same result as rescaling by the global max)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c0 + u < nchunk) {
-        const float wgt = wts[c0 + u][qi];
-        acc.x += v[u].x * wgt; acc.y += v[u].y * wgt; acc.z += v[u].z * wgt; acc.w += v[u].w * wgt;
-      }
+    for (int u = 0; u < 16; ++u) {
+      if (c0 + u >= nchunk || mc[u] == -INFINITY) continue;
+      const float Mn = fmaxf(M, mc[u]);
+      const float fa = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float fb = __builtin_amdgcn_exp2f(mc[u] - Mn);
+      L = L * fa + lc[u] * fb;
+      acc.x = acc.x * fa + v[u].x * fb; acc.y = acc.y * fa + v[u].y * fb;
+      acc.z = acc.z * fa + v[u].z * fb; acc.w = acc.w * fa + v[u].w * fb;
+      M = Mn;
     }
   }
   if (row < R) {
+    const float inv = 1.0f / L;
     u16x4 r;
-    r[0] = f2bf(acc.x); r[1] = f2bf(acc.y); r[2] = f2bf(acc.z); r[3] = f2bf(acc.w);
+    r[0] = f2bf(acc.x * inv); r[1] = f2bf(acc.y * inv); r[2] = f2bf(acc.z * inv); r[3] = f2bf(acc.w * inv);
     *reinterpret_cast<u16x4*>(o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD + d4) = r;
   }
 }
@@ -487,6 +493,13 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
     p.kind = 1;
     p.nqt = (R + 31) / 32;
     const int base = B * Hq * p.nqt;
+    if ((int64_t)base * ((S + 127) / 128) <= 512 && (S + 127) / 128 <= kMaxChunks) {
+      // one 32-key sub-tile per wave, up to two workgroups per CU
+      p.nchunk = (S + 127) / 128;
+      p.nsub = 1;
+      if (p.nchunk > 1) p.part_floats = (size_t)base * p.nchunk * (32 * HD + 64);
+      return p;
+    }
     int target = (256 + base - 1) / base;          // chunks wanted for ~256 workgroups
     if (target < 1) target = 1;
     int ck = (S + target - 1) / target;             // keys per chunk
@@ -523,14 +536,20 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
     const int64_t groups = (int64_t)B * Hq * p.nqt;
     float* part_o = part;
     float* part_ml = part ? part + groups * p.nchunk * (32 * HD) : nullptr;
-    attn_splitkv_bf16<<<dim3(p.nchunk, Hq * p.nqt, B), 256, 0, st>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
-        S, Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part_o, part_ml);
+    const dim3 grid(p.nchunk, Hq * p.nqt, B);
+    if (p.nsub == 1)
+      attn_splitkv_bf16<true><<<grid, 256, 0, st>>>(
+          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
+          S, Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part_o, part_ml);
+    else
+      attn_splitkv_bf16<false><<<grid, 256, 0, st>>>(
+          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
+          S, Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part_o, part_ml);
     if (p.nchunk > 1) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      attn_combine<<<dim3((unsigned)groups, 4), 256, 0, st>>>(part_o, part_ml, (uint16_t*)o, Hq,
-                                                              R, p.nqt, p.nchunk);
+      attn_combine<<<dim3((unsigned)groups, 32 / kCombRows), 32 * kCombRows, 0, st>>>(
+          part_o, part_ml, (uint16_t*)o, Hq, R, p.nqt, p.nchunk);
     }
   } else {
     attn_flash_bf16<<<dim3(p.nqt, Hq, B), 256, 0, st>>>(
