@@ -298,13 +298,13 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
     dllm_status st = gemm(c, refresh ? DLLM_K_REF_QKV : DLLM_K_STEP_QKV, EPI_QKV, h, d.d,
                           c.m->w_qkv[l], M, Nqkv, d.d, eq);
     if (st) return st;
+    if (refresh && l == d.L - 1) break;  // the last layer's attention and tail feed no K/V
     {
       ProfScope ps(refresh ? DLLM_K_REF_ATTN : DLLM_K_STEP_ATTN, c.st);
       HIP_TRY(launch_attention(d.dtype, ap, q, c.cache_k(l), c.cache_vt(l), o, d.B, d.Hq, d.Hkv,
                                R, d.S, d.Sp, d.D, c.at<float>(c.w.apart), c.at<int>(c.w.acnt),
                                c.st));
     }
-    if (refresh && l == d.L - 1) break;  // the last layer's tail feeds no K/V
     EpiArgs er;
     er.y = x; er.ldy = d.d;
     st = gemm(c, refresh ? DLLM_K_REF_O : DLLM_K_STEP_O, EPI_RESID, o, d.Hq * d.D, c.m->w_o[l], M,
