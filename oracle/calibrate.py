@@ -14,6 +14,8 @@ reach the threshold.  Procedure (a reading; the pages have no random-init models
    non-decreasing in s >= 0, so bisection finds the s_i where conf(s_i) = tau;
 3. the scale is the 30th percentile of {s_i}: at that scale 30 % of the positions
    reach the threshold.
+The stored workload scales refine this per step (tests/golden/make_logit_scales.py):
+the first-step scale brackets a bisection on the mean per-step fraction of block 0.
 """
 from __future__ import annotations
 
@@ -29,23 +31,29 @@ def conf_at_scale(z: np.ndarray, s: float) -> np.ndarray:
 
 
 def scale_for_threshold(z: np.ndarray, tau: float, iters: int = 60) -> np.ndarray:
-    """Per row, the scale s at which the row's confidence equals tau (bisection)."""
+    """Per row, the scale s at which the row's confidence equals tau (bisection).
+
+    A row whose maximum is attained k > 1 times never gets above 1/k, whatever the
+    scale; if that is below tau the row's scale is +inf (it never passes)."""
     z = np.asarray(z, dtype=np.float64)
-    lo = np.zeros(z.shape[0])
-    hi = np.ones(z.shape[0])
+    ties = (z == z.max(axis=1, keepdims=True)).sum(axis=1)
+    never = 1.0 / ties < tau
+    zz = z[~never]
+    lo = np.zeros(zz.shape[0])
+    hi = np.ones(zz.shape[0])
     while True:                                   # grow hi until every row reaches tau
-        c = conf_at_scale_rows(z, hi)
+        c = conf_at_scale_rows(zz, hi)
         if (c >= tau).all():
             break
         hi = np.where(c >= tau, hi, hi * 2.0)
-        if hi.max() > 1e9:
-            raise ValueError("a row never reaches the threshold (tied maxima?)")
     for _ in range(iters):
         mid = 0.5 * (lo + hi)
-        c = conf_at_scale_rows(z, mid)
+        c = conf_at_scale_rows(zz, mid)
         lo = np.where(c >= tau, lo, mid)
         hi = np.where(c >= tau, mid, hi)
-    return hi
+    out = np.full(z.shape[0], np.inf)
+    out[~never] = hi
+    return out
 
 
 def conf_at_scale_rows(z: np.ndarray, s: np.ndarray) -> np.ndarray:
