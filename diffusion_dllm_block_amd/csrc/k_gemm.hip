@@ -392,26 +392,27 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
 // ============================================================================
 // large bf16 GEMM (M >= 512, the refresh): 256x256 output tiles, 8 waves (two per
 // SIMD, so one can issue MFMAs while the other waits) each computing 128 rows x 64
-// columns with 32x32x16 MFMAs; 64-wide K stages double-buffered in LDS, the global
-// loads of stage s + 1 in flight while stage s is computed, and the LDS operands of
-// step kk + 1 read while step kk is in the MFMAs.  The epilogue runs one 128x128
+// columns with 32x32x16 MFMAs.  K advances in stages of DK columns held in a ring of
+// NSTG LDS slots that direct global->LDS loads fill NSTG - 1 stages ahead (one
+// barrier per stage, no staging registers), and the LDS operands of step kk + 1 are
+// read while step kk is in the MFMAs.  The epilogue runs one 128x128
 // quarter at a time through an fp32 LDS tile (the 128-column virtual tiles of the
 // other kernels).  Residual GEMMs with too few tiles split K and leave fp32 partials
 // [split][M][Nv] for the next RMSNorm.
 // ============================================================================
 constexpr int BG_T = 256;                                   // output tile (rows = cols)
 constexpr int BG_THREADS = 512;
-constexpr int BG_AB_BYTES = 2 * 2 * BG_T * TB_LD * 2;       // A and B, double-buffered
+constexpr int BG_DK = 64, BG_NSTG = 2;                      // K per stage, ring slots
+static_assert(BG_NSTG <= 4, "the wait counts cover at most two stages in flight");
+constexpr int BG_AB_BYTES = BG_NSTG * 2 * BG_T * BG_DK * 2;  // ring of A and B stages
 constexpr int BG_TILE_BYTES = 128 * TL * 4;                 // one 128x128 quarter, fp32
 constexpr int BG_SMEM = BG_AB_BYTES > BG_TILE_BYTES ? BG_AB_BYTES : BG_TILE_BYTES;
 
-template <int EPI>
+template <int EPI, int DK, int NSTG>
 __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv, int K,
     int kchunk, int splits, float* part, EpiArgs e) {
   extern __shared__ __attribute__((aligned(16))) unsigned char bg_smem[];
-  uint16_t* As = reinterpret_cast<uint16_t*>(bg_smem);
-  uint16_t* Bs = As + 2 * BG_T * TB_LD;
   float* tile = reinterpret_cast<float*>(bg_smem);
   const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
   const int m0 = tm * BG_T, vc0 = tn * BG_T;
@@ -420,33 +421,40 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
   const int w = tid >> 6, wm = w & 1, wn = w >> 1, l = tid & 63, lr = l & 31, g = l >> 5;
   const int kb = split * kchunk;
   const int ke = min(K, kb + kchunk);
-  const int nst = (ke - kb) / TB_K;
 
-  // loader: element e = tid + 512 i (i < 4) -> tile row e >> 3, 16-byte column e & 7;
-  // rows past M / columns past Nv load a clamped valid row (results discarded)
-  const int lrow = tid >> 3, lc8 = tid & 7;
-  const uint16_t* abase[4];
-  const uint16_t* bbase[4];
+  // K stages of DK columns in a ring of NSTG LDS slots, filled by direct global->LDS
+  // loads (no staging registers): each wave issues CPR/2 16-byte-per-lane loads of A
+  // and of B per stage, each writing 1 KB of LDS (64 / CPR tile rows).  Rows are stored
+  // unpadded with the 16-byte chunks XOR-swizzled by row, so the MFMA operand reads
+  // (32 rows at one k offset) spread over all banks.
+  constexpr int CPR = DK / 8;                  // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;                // tile rows per load instruction
+  constexpr int NI = 32 / RPI;                 // load instructions per wave per matrix
+  constexpr int HALF = BG_T * DK * 2;          // A (or B) bytes per stage
+  constexpr int STG = 2 * HALF;
+  const int nst = (ke - kb) / DK;
+  auto swz = [](int r) { return CPR == 4 ? ((r >> 1) & 3) : (r & (CPR - 1)); };
+  const uint16_t* asrc[NI];
+  const uint16_t* bsrc[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = lrow + 64 * i;
-    abase[i] = X + (int64_t)min(m0 + r, M - 1) * ldx + kb + 8 * lc8;
-    bbase[i] = W + (int64_t)wrow_of<EPI>(min(vc0 + r, Nv - 1), e.F) * K + kb + 8 * lc8;
+  for (int i = 0; i < NI; ++i) {
+    const int row = w * 32 + i * RPI + l / CPR;
+    const int c = (l % CPR) ^ swz(row);
+    asrc[i] = X + (int64_t)min(m0 + row, M - 1) * ldx + kb + c * 8;
+    bsrc[i] = W + (int64_t)wrow_of<EPI>(min(vc0 + row, Nv - 1), e.F) * K + kb + c * 8;
   }
-  u32x4 ra[4], rb[4];
-  auto load = [&](int st) {
+  auto issue = [&](int st) {
+    unsigned char* base = bg_smem + (st % NSTG) * STG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = *reinterpret_cast<const u32x4*>(abase[i] + st * TB_K);
-      rb[i] = *reinterpret_cast<const u32x4*>(bbase[i] + st * TB_K);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = lrow + 64 * i;
-      *reinterpret_cast<u32x4*>(&As[(buf * BG_T + r) * TB_LD + 8 * lc8]) = ra[i];
-      *reinterpret_cast<u32x4*>(&Bs[(buf * BG_T + r) * TB_LD + 8 * lc8]) = rb[i];
+    for (int i = 0; i < NI; ++i) {
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(asrc[i] + st * DK),
+          (__attribute__((address_space(3))) void*)(base + (w * 32 + i * RPI) * (DK * 2)), 16,
+          0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(bsrc[i] + st * DK),
+          (__attribute__((address_space(3))) void*)(base + HALF + (w * 32 + i * RPI) * (DK * 2)),
+          16, 0, 0);
     }
   };
   f32x16 acc[4][2];
@@ -454,22 +462,25 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  auto frag = [&](int buf, int kk, u32x4* a, u32x4* b) {
+  auto frag = [&](int slot, int kk, u32x4* a, u32x4* b) {
+    const unsigned char* base = bg_smem + slot * STG;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const u32x4*>(
-          &As[(buf * BG_T + wm * 128 + i * 32 + lr) * TB_LD + 16 * kk + 8 * g]);
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + i * 32 + lr, c = 2 * kk + g;
+      a[i] = *reinterpret_cast<const u32x4*>(base + r * (DK * 2) + ((c ^ swz(r)) * 16));
+    }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *reinterpret_cast<const u32x4*>(
-          &Bs[(buf * BG_T + wn * 64 + j * 32 + lr) * TB_LD + 16 * kk + 8 * g]);
+    for (int j = 0; j < 2; ++j) {
+      const int r = wn * 64 + j * 32 + lr, c = 2 * kk + g;
+      b[j] = *reinterpret_cast<const u32x4*>(base + HALF + r * (DK * 2) + ((c ^ swz(r)) * 16));
+    }
   };
-  auto compute = [&](int buf) {
+  auto compute = [&](int slot) {
     u32x4 a[2][4], b[2][2];
-    frag(buf, 0, a[0], b[0]);
+    frag(slot, 0, a[0], b[0]);
 #pragma unroll
-    for (int kk = 0; kk < TB_K / 16; ++kk) {
-      if (kk + 1 < TB_K / 16) frag(buf, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+    for (int kk = 0; kk < DK / 16; ++kk) {
+      if (kk + 1 < DK / 16) frag(slot, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -477,17 +488,25 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
           acc[i][j] = mfma32(as_bf16x8(a[kk & 1][i]), as_bf16x8(b[kk & 1][j]), acc[i][j]);
     }
   };
-
-  load(0);
-  store(0);
-  __syncthreads();
+  // s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left at their maximum)
+#define DLLM_VMWAIT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+  for (int st = 0; st < NSTG - 1 && st < nst; ++st) issue(st);
   for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) load(st + 1);
-    compute(buf);
-    if (st + 1 < nst) store(buf ^ 1);
-    __syncthreads();
+    // this wave's loads of stage st have landed once at most `ahead` later stages
+    // (2 * NI loads each) are still in flight; the barrier then covers every wave's
+    const int ahead = min(NSTG - 2, nst - 1 - st);
+    if (ahead >= 2) DLLM_VMWAIT(4 * NI);
+    else if (ahead == 1) DLLM_VMWAIT(2 * NI);
+    else DLLM_VMWAIT(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (st + NSTG - 1 < nst) issue(st + NSTG - 1);  // into the slot read at stage st - 1
+    compute(st % NSTG);
   }
+#undef DLLM_VMWAIT
+  __syncthreads();  // the epilogue tile below reuses the operand slots
 
   // epilogue, one 128x128 quarter (two waves) at a time
   for (int p = 0; p < 4; ++p) {
@@ -804,12 +823,13 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
   } else if (p.kind == GEMM_BIG) {
     static bool attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
     if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_big_bf16<EPI>),
+      hipError_t err = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&gemm_big_bf16<EPI, BG_DK, BG_NSTG>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, BG_SMEM);
       if (err != hipSuccess) return err;
       attr_set = true;
     }
-    gemm_big_bf16<EPI><<<dim3(p.ntn, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
+    gemm_big_bf16<EPI, BG_DK, BG_NSTG><<<dim3(p.ntn, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e);
   } else {
     gemm_tiled_bf16<EPI><<<dim3(p.ntn, p.ntm, p.splits), 256, 0, st>>>(
