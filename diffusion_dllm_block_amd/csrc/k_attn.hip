@@ -341,36 +341,38 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // K and Vt tiles of the next 64 keys are loaded into registers while the current
+  // tile is computed (branch-free: K rows past S read row S-1, whose scores are masked;
+  // Vt keys past S read as zero)
   const int ntile = (S + FK - 1) / FK;
+  u32x4 kreg[4], vreg[4];
+  auto load_tile = [&](int kt) {
+    const int kbase = kt * FK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int r = e >> 4, c8 = e & 15;  // K: 64 rows x 16 chunks
+      kreg[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)min(kbase + r, S - 1) * HD + 8 * c8);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = threadIdx.x + 256 * i;
+      const int r = e >> 3, c8 = e & 7;   // Vt: 128 rows x 8 chunks of 8 keys
+      vreg[i] = __builtin_bit_cast(u32x4, load8_masked(vb + (int64_t)r * Sp, kbase + 8 * c8, S, Sp));
+    }
+  };
+  load_tile(0);
   for (int kt = 0; kt < ntile; ++kt) {
     const int kbase = kt * FK;
-    __syncthreads();
-    // stage K tile: 64 rows x 128 -> 1024 x 16B, 4 per thread
+    __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = threadIdx.x + 256 * i;
-      int r = e >> 4, c8 = e & 15;
-      u32x4 val = u32x4{};
-      if (kbase + r < S) val = *reinterpret_cast<const u32x4*>(kb + (int64_t)(kbase + r) * HD + 8 * c8);
-      *reinterpret_cast<u32x4*>(&Ks[r * KS_LD + 8 * c8]) = val;
-    }
-    // stage Vt tile: 128 rows x 64 keys -> 1024 x 16B, 4 per thread
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int e = threadIdx.x + 256 * i;
-      int r = e >> 3, c8 = e & 7;
-      int kk = kbase + 8 * c8;
-      u32x4 val = u32x4{};
-      if (kk + 8 <= S) {
-        val = *reinterpret_cast<const u32x4*>(vb + (int64_t)r * Sp + kk);
-      } else if (kk < S) {
-        uint16_t tmp[8];
-        for (int e2 = 0; e2 < 8; ++e2) tmp[e2] = (kk + e2 < S) ? vb[(int64_t)r * Sp + kk + e2] : 0;
-        val = *reinterpret_cast<u32x4*>(tmp);
-      }
-      *reinterpret_cast<u32x4*>(&Vs[r * VS_LD + 8 * c8]) = val;
+      const int e = threadIdx.x + 256 * i;
+      *reinterpret_cast<u32x4*>(&Ks[(e >> 4) * KS_LD + 8 * (e & 15)]) = kreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[(e >> 3) * VS_LD + 8 * (e & 7)]) = vreg[i];
     }
     __syncthreads();
+    if (kt + 1 < ntile) load_tile(kt + 1);
 
     float p[2][16];
     float tmax = -INFINITY;
