@@ -139,6 +139,63 @@ __global__ __launch_bounds__(kFoldThreads) void fold_norm_kernel(float* x, int R
   }
 }
 
+// Embedding gather + RMSNorm in one pass, the row in registers (the layout of
+// fold_norm_kernel): x[j] = embed[token] (fp32), h[j] = rmsnorm(x[j]) * g.
+template <typename T, int NJ>
+__global__ __launch_bounds__(kFoldThreads) void embed_norm_fast(const int* tokens, int S, int r0,
+                                                               int R, const T* embed, const T* g,
+                                                               float eps, int d, int V, float* x,
+                                                               T* h) {
+  __shared__ float red[kFoldThreads / kWave];
+  const int j0 = blockIdx.x;
+  const int b = j0 / R, i = j0 % R;
+  int tok = tokens[(int64_t)b * S + r0 + i];
+  tok = min(max(tok, 0), V - 1);  // ids outside [0, V) are not valid input; never read out of bounds
+  const T* er = embed + (int64_t)tok * d;
+  const int tid = threadIdx.x;
+  float v[NJ][4], gv[NJ][4];
+  bool ok[NJ];
+  int col[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    col[jj] = 4 * tid + 4096 * jj;
+    ok[jj] = col[jj] < d;
+    col[jj] = ok[jj] ? col[jj] : 0;  // clamped, never stored
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[jj][u] = Elt<T>::load(er, col[jj] + u);
+      gv[jj][u] = Elt<T>::load(g, col[jj] + u);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj)
+    if (ok[jj]) ss += v[jj][0] * v[jj][0] + v[jj][1] * v[jj][1] + v[jj][2] * v[jj][2] + v[jj][3] * v[jj][3];
+  ss = wave_sum(ss);
+  if ((tid & (kWave - 1)) == 0) red[tid / kWave] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int k = 0; k < kFoldThreads / kWave; ++k) tot += red[k];
+  const float r = 1.0f / sqrtf(tot / (float)d + eps);
+  float* xr = x + (int64_t)j0 * d;
+  T* hr = h + (int64_t)j0 * d;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    if (!ok[jj]) continue;
+    const int c = col[jj];
+    *reinterpret_cast<float4*>(xr + c) = make_float4(v[jj][0], v[jj][1], v[jj][2], v[jj][3]);
+    float o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = (v[jj][u] * r) * gv[jj][u];
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<u16x4*>(hr + c) = u16x4{f2bf(o[0]), f2bf(o[1]), f2bf(o[2]), f2bf(o[3])};
+    } else {
+      *reinterpret_cast<float4*>(hr + c) = make_float4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* x, int Rin, int Kout, const T* g,
                                                       float eps, int d, T* h, PartView pv) {
@@ -163,6 +220,18 @@ hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R,
                              const void* embed, const void* g, float eps, int d, int V, float* x,
                              void* h, hipStream_t st) {
   dim3 grid(B * R);
+  if (d % 4 == 0 && d <= 8192) {
+#define DLLM_EMB(TT, NJV)                                                                   \
+  embed_norm_fast<TT, NJV><<<grid, kFoldThreads, 0, st>>>(tokens, S, r0, R, (const TT*)embed, \
+                                                          (const TT*)g, eps, d, V, x, (TT*)h)
+    if (dtype == F32) {
+      if (d <= 4096) DLLM_EMB(float, 1); else DLLM_EMB(float, 2);
+    } else {
+      if (d <= 4096) DLLM_EMB(uint16_t, 1); else DLLM_EMB(uint16_t, 2);
+    }
+#undef DLLM_EMB
+    return hipGetLastError();
+  }
   if (dtype == F32)
     embed_norm_kernel<float><<<grid, 256, 0, st>>>(tokens, S, r0, R, (const float*)embed,
                                                    (const float*)g, eps, d, V, x, (float*)h);

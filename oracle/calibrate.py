@@ -14,8 +14,7 @@ reach the threshold.  Procedure (a reading; the pages have no random-init models
    non-decreasing in s >= 0, so bisection finds the s_i where conf(s_i) = tau;
 3. the scale is the 30th percentile of {s_i}: at that scale 30 % of the positions
    reach the threshold.
-The stored workload scales refine this per step (tests/golden/make_logit_scales.py):
-the first-step scale brackets a bisection on the mean per-step fraction of block 0.
+tests/golden/make_logit_scales.py applies it to each 8B/7B workload.
 """
 from __future__ import annotations
 

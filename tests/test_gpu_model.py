@@ -179,3 +179,44 @@ def test_generate_properties_llada_shape_two_blocks(lib):
     assert np.array_equal(res[0], res[1])
     del model
     torch.cuda.empty_cache()
+
+
+FULL_SIZE = ["llada8b_dual_p1000_g1024", "llada8b_prefix_p256_g256", "dream7b_dual_b8_p512_g512"]
+
+
+@pytest.mark.parametrize("name", FULL_SIZE)
+def test_first_step_full_size_matches_oracle_sample(lib, name):
+    """The full 8B/7B shapes at their calibrated scale: after the prefill, the first
+    cached step's logits at the oracle's sampled (row, id) pairs, its argmax and its
+    confidence.  The sample was written by tests/golden/make_logit_scales.py from the
+    oracle (float32 with bf16 storage rounding), so the bound is the bf16 one: logit
+    errors within 2e-2 of the row's largest logit, argmax equal wherever the top-2 gap
+    exceeds twice the observed error, confidence within conf * (exp(2 dl) - 1)."""
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", f"first_step_{name}.json")
+    if not os.path.exists(path):
+        pytest.skip(f"no oracle sample for {name}")
+    fx = json.load(open(path))
+    wl = synth.with_scale(synth.WORKLOADS[name], fx["logit_scale"])
+    model = Model.synthetic(lib, wl)
+    s = Session(model, synth.make_prompt(wl), wl.gen_len, wl.block_len, wl.threshold,
+                wl.cache_mode)
+    s.prefill()
+    o = s.step(0)
+    torch.cuda.synchronize()
+    V = wl.model.vocab
+    lg = o["logits"].cpu().numpy().reshape(wl.batch, wl.block_len, V)[0].astype(np.float64)
+    conf = o["conf"].cpu().numpy().reshape(wl.batch, wl.block_len)[0]
+    arg = o["argmax"].cpu().numpy().reshape(wl.batch, wl.block_len)[0]
+    scale = fx["logit_scale"]
+    for row in fx["rows"]:
+        r, ids = row["row"], np.array(row["ids"])
+        ref = scale * np.array(row["z"])
+        dl = np.max(np.abs(lg[r, ids] - ref))
+        assert dl <= 2e-2 * np.abs(ref).max(), f"row {r}: logit error {dl}"
+        if ref[0] - ref[1] > 2 * dl + 1e-6:
+            assert arg[r] == row["argmax"], f"row {r}"
+        assert abs(conf[r] - row["conf"]) <= row["conf"] * np.expm1(2 * dl) + 1e-6, f"row {r}"
+    del model
+    torch.cuda.empty_cache()
