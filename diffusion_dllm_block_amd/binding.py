@@ -24,7 +24,7 @@ STATUS = {0: "DLLM_OK", -1: "DLLM_E_NULL", -2: "DLLM_E_SHAPE", -3: "DLLM_E_UNSUP
 
 KERNEL_CLASSES = ["EMBED_NORM", "RMSNORM", "STEP_QKV", "STEP_ATTN", "STEP_O", "STEP_GATE_UP",
                   "STEP_DOWN", "LM_HEAD", "CONF_UNMASK", "REF_QKV", "REF_ATTN", "REF_O",
-                  "REF_GATE_UP", "REF_DOWN"]
+                  "REF_GATE_UP", "REF_DOWN", "SPLIT_REDUCE"]
 
 
 class ModelDesc(C.Structure):

@@ -766,10 +766,6 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   return p;
 }
 
-hipError_t launch_gemm_only(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
-                            const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
-                            int* counters, hipStream_t st);
-
 static int num_cus() {
   static int n = 0;
   if (n == 0) {

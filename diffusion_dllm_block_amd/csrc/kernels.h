@@ -74,9 +74,14 @@ struct GemmPlan {
 };
 
 GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi);
+// launch_gemm = launch_gemm_only + (skinny, non-residual) launch_reduce_epilogue
 hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
                        const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
                        int* counters, hipStream_t st);
+hipError_t launch_gemm_only(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
+                            const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
+                            int* counters, hipStream_t st);
+hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 struct AttnPlan {

@@ -247,9 +247,15 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
     return fail(DLLM_E_WORKSPACE, "internal: GEMM plan exceeds the workspace plan");
   if (c.pend.splits)
     return fail(DLLM_E_STATE, "internal: pending residual partials not consumed");
-  ProfScope ps(cls, c.st);
-  HIP_TRY(launch_gemm(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, e, c.at<float>(c.w.gpart),
-                      c.at<int>(c.w.gcnt), c.st));
+  {
+    ProfScope ps(cls, c.st);
+    HIP_TRY(launch_gemm_only(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, e, c.at<float>(c.w.gpart),
+                             c.at<int>(c.w.gcnt), c.st));
+  }
+  if (p.kind == GEMM_SKINNY && epi != EPI_RESID) {
+    ProfScope ps(DLLM_K_SPLIT_REDUCE, c.st);
+    HIP_TRY(launch_reduce_epilogue(epi, p.view(c.at<float>(c.w.gpart), M, Nv), e, c.st));
+  }
   if (p.deferred && epi == EPI_RESID) {
     c.pend.splits = p.splits;
     c.pend.view = p.view(c.at<float>(c.w.gpart), M, Nv);

@@ -220,12 +220,15 @@ const char* dllm_last_error(void);
 /* Per-kernel-class timing with HIP events on the launching stream.  Select one class
  * (or -1 for none); every later launch of that class is bracketed by two events;
  * dllm_profile_read() synchronises on the recorded events and returns the number of
- * launches and their summed duration, then clears the record.                       */
+ * launches and their summed duration, then clears the record.  A GEMM class times the
+ * GEMM kernel alone; the split-K reduction that applies a step GEMM's epilogue (QKV,
+ * gate/up, LM head) is the class SPLIT_REDUCE.                                          */
 typedef enum {
   DLLM_K_NONE = -1,
   DLLM_K_EMBED_NORM = 0, DLLM_K_RMSNORM, DLLM_K_STEP_QKV, DLLM_K_STEP_ATTN, DLLM_K_STEP_O,
   DLLM_K_STEP_GATE_UP, DLLM_K_STEP_DOWN, DLLM_K_LM_HEAD, DLLM_K_CONF_UNMASK,
   DLLM_K_REF_QKV, DLLM_K_REF_ATTN, DLLM_K_REF_O, DLLM_K_REF_GATE_UP, DLLM_K_REF_DOWN,
+  DLLM_K_SPLIT_REDUCE,
   DLLM_K_COUNT
 } dllm_kernel_class;
 dllm_status dllm_profile_select(int32_t kernel_class);
