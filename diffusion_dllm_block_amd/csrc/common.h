@@ -64,6 +64,53 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Lane permutes on the DPP path (a VALU operand modifier, no LDS crossbar).  Controls:
+// 0xB1 = quad_perm [1,0,3,2] (lane ^ 1), 0x4E = quad_perm [2,3,0,1] (lane ^ 2),
+// 0x141 = row_half_mirror (lane 7 - i within 8), 0x140 = row_mirror (15 - i within 16).
+// All four are full permutations inside a 16-lane row, so every source lane is valid.
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Reduce within aligned groups of G = 2, 4, 8 or 16 consecutive lanes: afterwards every
+// lane of a group holds op over the group.  op must be commutative (max, min, +), so
+// partner lanes compute bit-identical values.
+template <int G, typename V, typename Op>
+__device__ __forceinline__ V group_reduce(V v, Op op) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group size");
+  v = op(v, dpp<0xB1>(v));
+  if constexpr (G >= 4) v = op(v, dpp<0x4E>(v));
+  if constexpr (G >= 8) v = op(v, dpp<0x141>(v));
+  if constexpr (G >= 16) v = op(v, dpp<0x140>(v));
+  return v;
+}
+
+// Whole-wave reduction: 16-lane rows on the DPP path, then the four row results read
+// into scalar registers and combined in a fixed order ((r0, r1), (r2, r3)).  Every lane
+// receives the same value.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  auto mx = [](float a, float b) { return fmaxf(a, b); };
+  v = group_reduce<16>(v, mx);
+  return fmaxf(fmaxf(readlane_f(v, 0), readlane_f(v, 16)), fmaxf(readlane_f(v, 32), readlane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = group_reduce<16>(v, [](float a, float b) { return a + b; });
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = group_reduce<16>(v, [](int a, int b) { return min(a, b); });
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
 // Cross-workgroup hand-off of split partial results without cache-wide maintenance.
 // Partials are written with device-coherent stores (relaxed agent-scope atomics: the
 // store carries sc1 and is acknowledged once it is visible to every XCD) and read back

@@ -7,11 +7,12 @@
 // techwalker.com explainer, "Solving the quality loss of parallel decoding").
 //
 // Two passes.  Pass 1, grid (nsplit, rows): each workgroup streams one slice of one row
-// with 16-byte loads and keeps a per-thread online (max, argmax, sum exp) triple; the
-// triples are merged in a fixed order (thread-sequential, wave butterfly, waves in
-// order) into a per-(row, slice) partial.  Pass 2, one workgroup per sequence, merges
-// each row's slices in slice order (one lane per row) and runs the unmask rule with
-// wave ballots.  No atomics: results are bit-identical from run to run.
+// with 16-byte loads (all of a thread's loads in flight together), takes the slice's
+// maximum, then the sum of exp(z - max), and writes a per-(row, slice) (max, sum,
+// argmax) triple.  Pass 2, one workgroup per sequence, merges each row's slice triples
+// (a few lanes per row, then a lane butterfly) and runs the unmask rule with wave
+// ballots.  Cross-lane steps use DPP lane permutes and fixed combination orders; there
+// are no atomics, so results are bit-identical from run to run.
 #include <algorithm>
 
 #include "common.h"
@@ -84,82 +85,153 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
   }
 }
 
-__device__ __forceinline__ Trip wave_merge(Trip t) {
-  for (int o = 1; o < kWave; o <<= 1) {
-    Trip u;
-    u.m = __shfl_xor(t.m, o, kWave);
-    u.s = __shfl_xor(t.s, o, kWave);
-    u.idx = __shfl_xor(t.idx, o, kWave);
-    // combine in a lane-independent order: lower lane group first
-    bool lower = (threadIdx.x & o) == 0;
-    t = lower ? merge(t, u) : merge(u, t);
-  }
-  return t;
-}
-
 constexpr int kConfThreads = 256;
 constexpr int kConfMaxParts = 2048;  // K * nsplit per sequence (finalize stages them in LDS)
 constexpr int kConfMaxSplit = 64;
 
-// Pass 1, one workgroup per (slice, row).  A slice is IT * 2048 consecutive ids (the
-// last one shorter); each thread issues all of its IT 8-element loads before folding
-// them, so a slice costs one memory round trip.  Writes the slice's (max, sum, argmax).
+// Workgroup merge of per-thread (max m, sum s of exp(z - m)) pairs: the slice maximum M,
+// the sum rescaled to M, and the lowest id reaching M, which only threads with m == M
+// look for (find_idx returns a thread's lowest such id).  All threads must call it.
+template <typename F>
+__device__ __forceinline__ Trip block_merge(float m, float s, F find_idx, float* rm, float* rs,
+                                            int* ri) {
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  constexpr int NW = kConfThreads / kWave;
+  const float wm = wave_max_dpp(m);
+  if (lane == 0) rm[w] = wm;
+  __syncthreads();
+  float M = rm[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, rm[i]);
+  if (M == -INFINITY) return Trip{-INFINITY, 0.f, 0x7fffffff};  // uniform: empty slice
+  const float sr = (m == -INFINITY) ? 0.f : s * __builtin_amdgcn_exp2f((m - M) * kLog2e);
+  const int idx = (m == M) ? find_idx(M) : 0x7fffffff;
+  const float ws = wave_sum_dpp(sr);
+  const int wi = wave_min_dpp(idx);
+  if (lane == 0) { rs[w] = ws; ri[w] = wi; }
+  __syncthreads();
+  Trip r{M, rs[0], ri[0]};
+#pragma unroll
+  for (int i = 1; i < NW; ++i) { r.s += rs[i]; r.idx = min(r.idx, ri[i]); }
+  return r;
+}
+
+// Pass 1, one workgroup per (slice, row).  A slice is chunk consecutive ids (the last one
+// shorter).  When chunk == IT * 2048 (the usual plan) each thread holds its IT groups of 8
+// values in registers: maximum first, then one exp per value, and the argmax search only
+// in threads that hold the slice maximum.  Longer slices (very large vocabularies) fold
+// online, one group of 8 at a time.  The mask id never counts.
 template <typename T, int IT>
 __global__ __launch_bounds__(kConfThreads) void conf_partials_kernel(
     const T* __restrict__ logits, int V, int mask_id, int nsplit, int chunk, float* pm,
     float* ps, int* pi) {
-  __shared__ Trip red[kConfThreads / kWave];
+  __shared__ float rm[kConfThreads / kWave], rs[kConfThreads / kWave];
+  __shared__ int ri[kConfThreads / kWave];
   const int split = blockIdx.x, row = blockIdx.y;
   const int lo = split * chunk;
   const int hi = min(V, lo + chunk);
   const T* zr = logits + (int64_t)row * V;
   const int tid = threadIdx.x;
+  constexpr int SPAN = IT * kConfThreads * 8;
 
-  Trip t{-INFINITY, 0.f, 0x7fffffff};
-  if ((V % 8) == 0) {  // rows and slices start on 16-byte boundaries
-    for (int base = lo; base < hi; base += IT * kConfThreads * 8) {
-      float v[IT][8];
+  Trip t;
+  if ((V % 8) == 0 && chunk == SPAN) {
+    float v[IT][8];
 #pragma unroll
-      for (int j = 0; j < IT; ++j)  // clamped in-row address; values past hi are dropped
-        load8<T>(zr + min(base + (j * kConfThreads + tid) * 8, V - 8), v[j]);
+    for (int j = 0; j < IT; ++j)  // clamped in-row address; values past hi are dropped
+      load8<T>(zr + min(lo + (j * kConfThreads + tid) * 8, V - 8), v[j]);
+    if (hi - lo < SPAN || (lo <= mask_id && mask_id < hi)) {  // uniform: ragged or mask slice
 #pragma unroll
-      for (int j = 0; j < IT; ++j) {
-        const int i = base + (j * kConfThreads + tid) * 8;
-        fold(t, v[j], min(max(hi - i, 0), 8), i, mask_id);
+      for (int j = 0; j < IT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int i = lo + (j * kConfThreads + tid) * 8 + e;
+          if (i >= hi || i == mask_id) v[j][e] = -INFINITY;
+        }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < IT; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, v[j][e]);
+    float s = 0.f;
+    if (m != -INFINITY) {
+      const float ml = m * kLog2e;
+#pragma unroll
+      for (int j = 0; j < IT; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, -ml));
+    }
+    auto find = [&](float M) {
+      int best = 0x7fffffff;
+#pragma unroll
+      for (int j = IT - 1; j >= 0; --j)
+#pragma unroll
+        for (int e = 7; e >= 0; --e)
+          if (v[j][e] == M) best = lo + (j * kConfThreads + tid) * 8 + e;
+      return best;
+    };
+    t = block_merge(m, s, find, rm, rs, ri);
+  } else {
+    Trip u{-INFINITY, 0.f, 0x7fffffff};
+    if ((V % 8) == 0) {
+      for (int base = lo; base < hi; base += SPAN) {
+        float v[IT][8];
+#pragma unroll
+        for (int j = 0; j < IT; ++j)
+          load8<T>(zr + min(base + (j * kConfThreads + tid) * 8, V - 8), v[j]);
+#pragma unroll
+        for (int j = 0; j < IT; ++j) {
+          const int i = base + (j * kConfThreads + tid) * 8;
+          fold(u, v[j], min(max(hi - i, 0), 8), i, mask_id);
+        }
+      }
+    } else {
+      for (int i = lo + tid; i < hi; i += kConfThreads) {
+        float v[8];
+        v[0] = Elt<T>::load(zr, i);
+        fold(u, v, 1, i, mask_id);
       }
     }
-  } else {
-    for (int i = lo + tid; i < hi; i += kConfThreads) {
-      float v[8];
-      v[0] = Elt<T>::load(zr, i);
-      fold(t, v, 1, i, mask_id);
-    }
+    t = block_merge(u.m, u.s, [&](float) { return u.idx; }, rm, rs, ri);
   }
-  t = wave_merge(t);
-  const int w = tid / kWave, lane = tid % kWave;
-  if (lane == 0) red[w] = t;
-  __syncthreads();
   if (tid == 0) {
-    Trip a = red[0];
-    for (int i = 1; i < kConfThreads / kWave; ++i) a = merge(a, red[i]);
     const int64_t o = (int64_t)row * nsplit + split;
-    pm[o] = a.m;
-    ps[o] = a.s;
-    pi[o] = a.idx;
+    pm[o] = t.m;
+    ps[o] = t.s;
+    pi[o] = t.idx;
   }
 }
 
 // Pass 2, one workgroup per sequence: stage its K * nsplit partials in LDS (all loads
-// issued together), merge each row's slices in slice order (lane i of wave 0 = block
-// position i), then apply the threshold rule with wave ballots.
+// issued together, the block's tokens read first), merge each row's slices with G lanes
+// per row (G = 8 for K <= 32, else 4; slices sp = g, g + G, ... per lane, then a lane
+// butterfly), and apply the threshold rule with wave ballots (lane i = block position i).
+template <int G>
+__device__ __forceinline__ Trip merge_lanes(Trip a) {
+  auto step = [&](auto perm) {
+    Trip o{perm(a.m), perm(a.s), 0};
+    o.idx = __float_as_int(perm(__int_as_float(a.idx)));
+    a = merge(a, o);
+  };
+  step([](float x) { return dpp<0xB1>(x); });
+  if constexpr (G >= 4) step([](float x) { return dpp<0x4E>(x); });
+  if constexpr (G >= 8) step([](float x) { return dpp<0x141>(x); });
+  return a;
+}
+
 __global__ __launch_bounds__(kConfThreads) void conf_finalize_kernel(
     int K, int nsplit, int mask_id, float tau, const float* pm, const float* ps, const int* pi,
     int* tokens, int ld_tokens, float* conf, int* argmax, int* n_unmasked, int* remaining,
     int* unmasked_idx) {
   __shared__ float fm[kConfMaxParts], fs[kConfMaxParts];
   __shared__ int fi[kConfMaxParts];
+  __shared__ float rowc[kWave];
+  __shared__ int rowi[kWave];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  int* tb = tokens + (int64_t)b * ld_tokens;
+  const int tok = (tid < K) ? tb[tid] : 0;
   const int nparts = K * nsplit;
   const int64_t pbase = (int64_t)b * K * nsplit;
   for (int e0 = 0; e0 < nparts; e0 += kConfThreads * 8) {
@@ -179,26 +251,31 @@ __global__ __launch_bounds__(kConfThreads) void conf_finalize_kernel(
     }
   }
   __syncthreads();
+  {
+    const int G = (K <= kConfThreads / 8) ? 8 : 4;
+    const int row = tid / G, g = tid % G;
+    Trip a{-INFINITY, 0.f, 0x7fffffff};
+    if (row < K)
+      for (int sp = g; sp < nsplit; sp += G) {
+        const int e = row * nsplit + sp;
+        a = merge(a, Trip{fm[e], fs[e], fi[e]});
+      }
+    a = (G == 8) ? merge_lanes<8>(a) : merge_lanes<4>(a);
+    if (g == 0 && row < K) {
+      const float c = 1.0f / a.s;
+      rowc[row] = c;
+      rowi[row] = a.idx;
+      conf[b * K + row] = c;
+      argmax[b * K + row] = a.idx;
+    }
+  }
+  __syncthreads();
   if (tid >= kWave) return;
 
   const int i = tid;
   const bool active = i < K;
-  float c = 0.f;
-  int am = 0;
-  if (active) {
-    const int r = b * K + i;
-    Trip a{-INFINITY, 0.f, 0x7fffffff};
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const int e = i * nsplit + sp;
-      a = merge(a, Trip{fm[e], fs[e], fi[e]});
-    }
-    c = 1.0f / a.s;
-    am = a.idx;
-    conf[r] = c;
-    argmax[r] = am;
-  }
-  int* tb = tokens + (int64_t)b * ld_tokens;
-  const int tok = active ? tb[i] : 0;
+  const float c = active ? rowc[i] : 0.f;
+  const int am = active ? rowi[i] : 0;
   const bool masked = active && tok == mask_id;
   const bool sel = masked && c >= tau;
   uint64_t ballot_sel = __ballot(sel);
@@ -229,13 +306,13 @@ __global__ __launch_bounds__(kConfThreads) void conf_finalize_kernel(
   }
 }
 
-// Slices of IT * 2048 ids with IT in {1, 2, 4, 8}: about 1024 workgroups in total, at
+// Slices of IT * 2048 ids with IT in {1, 2, 4, 8}: about 512 workgroups in total, at
 // most kConfMaxSplit slices per row and kConfMaxParts partials per sequence.
 ConfPlan conf_plan(int rows, int V, int B) {
   ConfPlan p;
   const int K = rows / (B > 0 ? B : 1);
   const int per = kConfThreads * 8;
-  int want = (1024 + rows - 1) / rows;  // slices per row for ~1024 workgroups
+  int want = (512 + rows - 1) / rows;  // slices per row for ~512 workgroups
   if (want < 1) want = 1;
   int it = 1;
   while (it < 8 && (int64_t)it * per * want < V) it *= 2;

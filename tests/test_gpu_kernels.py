@@ -71,14 +71,18 @@ CONF_CASES = [
     ("ragged_vocab_scalar_path", 3, 7, 1001, 10.0, "f32", 0.7),
     ("k64_small_vocab", 2, 64, 4096, 9.0, "bf16", 0.9),
     ("k1", 4, 1, 640, 6.0, "f32", 1.0),
+    # mask id inside a full slice (LLaDA's id), not in the ragged last one
+    ("mask_mid_vocab_bf16", 2, 32, 126464, 12.0, "bf16", 1.0, 126336),
+    # slices longer than one pass of the workgroup (vocabulary > 32 slices of 16384)
+    ("huge_vocab_looped_slices", 1, 64, 600000, 12.0, "f32", 1.0),
 ]
 
 
 @pytest.mark.parametrize("case", CONF_CASES, ids=[c[0] for c in CONF_CASES])
 @pytest.mark.parametrize("tau", [0.9, 0.5, 1.5, 0.0])
 def test_confidence_unmask_parity(lib, case, tau):
-    name, B, K, V, boost, ldt, frac = case
-    mask_id = V - 1
+    name, B, K, V, boost, ldt, frac = case[:7]
+    mask_id = case[7] if len(case) > 7 else V - 1
     z = synth.boosted_logits(43, B * K, V, boost, ldt)
     zf = synth.bf16_bits_to_fp32(z) if ldt == "bf16" else z
     dev = dev_bf16(z) if ldt == "bf16" else dev_f32(z)
@@ -111,6 +115,29 @@ def test_confidence_unmask_parity(lib, case, tau):
     assert np.all((nun >= 1) | (masked.sum(1) == 0))
     assert np.all(nun + rem == masked.sum(1))
     assert np.all(got_tok[~masked] == toks[~masked])
+
+
+@pytest.mark.parametrize("ldt", ["bf16", "f32"])
+def test_confidence_tied_maxima(lib, ldt):
+    """Logits on a coarse grid: every row's maximum is reached at many ids, and the
+    argmax must be the lowest of them (the mask id excluded even when it ties)."""
+    B, K, V = 2, 32, 126464
+    r = np.random.default_rng(7)
+    zf = np.clip(np.round(r.standard_normal((B * K, V)) * 2) / 2, -4.0, 2.0).astype(np.float32)
+    mask_id = 126336
+    zf[:, mask_id] = 2.0
+    if ldt == "bf16":
+        z = (zf.view(np.uint32) >> 16).astype(np.uint16)   # exact: the grid values are bf16
+        dev = dev_bf16(z)
+    else:
+        dev = dev_f32(zf)
+    toks = np.full((B, K), mask_id)
+    _, conf, arg, nun, rem, _ = run_conf(lib, dev, bd.F32 if ldt == "f32" else bd.BF16,
+                                         B, K, V, mask_id, 0.9, toks)
+    rc, ra = decode.confidence_argmax(zf.astype(np.float64), mask_id)
+    assert np.array_equal(arg.reshape(-1), ra)
+    assert np.max(np.abs(conf.reshape(-1) - rc) / rc) < 2e-5
+    assert np.all(nun == 1) and np.all(rem == K - 1)
 
 
 # ------------------------------------------------------------------ attention
