@@ -93,6 +93,23 @@ __device__ __forceinline__ V group_reduce(V v, Op op) {
   return v;
 }
 
+// Combine each lane with its partner lane ^ 16 or lane ^ 32 (gfx950 v_permlane16_swap /
+// v_permlane32_swap of a register with itself).  The swap returns, in every lane, the
+// pair's two values in lane order, so a commutative op gives both partners the same
+// bits, as an xor shuffle would, without the LDS crossbar.
+template <typename Op>
+__device__ __forceinline__ float xor16_combine(float x, Op op) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32_combine(float x, Op op) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float fmax_op(float a, float b) { return fmaxf(a, b); }
+__device__ __forceinline__ float add_op(float a, float b) { return a + b; }
+
 // Whole-wave reduction: 16-lane rows on the DPP path, then the four row results read
 // into scalar registers and combined in a fixed order ((r0, r1), (r2, r3)).  Every lane
 // receives the same value.

@@ -65,11 +65,12 @@ __device__ __forceinline__ bf16x8 load8_masked(const uint16_t* row, int k, int S
 //   O^T (16 dims x 16 queries) += Vt . P^T with k = the 32 keys in natural order: the
 //       lane's 8 scores are exactly its B operand, and the Vt operand of lane (d, j) is
 //       keys 8j .. 8j+7 of row d.
-// A query's 32 keys live in the 4 lanes l%16 + 16j, so its max and sum need two xor
-// shuffles.  Waves are merged through LDS in a fixed order; with several chunks the
+// A query's 32 keys live in the 4 lanes l%16 + 16j, so its max and sum need two partner
+// combines (lane ^ 16, lane ^ 32).  Waves are merged through LDS in a fixed order; with several chunks the
 // workgroup writes unnormalised partials (O, m, l) and attn_combine merges them.
 // ============================================================================
 constexpr int SK_OLD = HD + 4;  // LDS row stride (floats) of the per-wave O tiles
+constexpr int QS_LD = HD + 8;   // LDS row stride (elements) of the staged Q tile
 
 struct KVTile16 {
   u32x4 k[2][4];  // [tau][k-step]: K row of key 8(i/4) + 4 tau + i%4, dims 32 s + 8j
@@ -111,17 +112,36 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
   const int kpw = 32 * nsub;
   const int wkey0 = chunk * 4 * kpw + w * kpw;
 
-  // Q^T operands: [query tile qq][k-step]: query 16 qq + li, dims 32 s + 8j .. +8
-  u32x4 qf[2][4];
+  // The workgroup's Q tile (32 rows x 128) is read from memory once, two 16-byte pieces
+  // per thread (rows >= R clamped: computed, never stored), issued before the first K/Vt
+  // tile so that both are in flight together, then staged in LDS for the 4 waves.  The
+  // staging area is the start of osum, which is written only after the products.
+  const uint16_t* qh = q + ((int64_t)b * Hq + hq) * R * HD;
+  u32x4 qg[2];
 #pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int qrow = min(qt * 32 + 16 * qq + li, R - 1);  // rows >= R: computed, never stored
-    const uint16_t* qp = q + (((int64_t)b * Hq + hq) * R + qrow) * HD + 8 * j;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) qf[qq][st] = *reinterpret_cast<const u32x4*>(qp + 32 * st);
+  for (int u = 0; u < 2; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    qg[u] = *reinterpret_cast<const u32x4*>(qh + (int64_t)min(qt * 32 + (e >> 4), R - 1) * HD +
+                                            8 * (e & 15));
   }
   const uint16_t* kbase = k + ((int64_t)b * Hkv + hkv) * Sp * HD;
   const uint16_t* vbase = vt + ((int64_t)b * Hkv + hkv) * HD * Sp;
+  KVTile16 ta;
+  load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(&osum[0][0][0]);  // [32][QS_LD]
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    *reinterpret_cast<u32x4*>(&qs[(e >> 4) * QS_LD + 8 * (e & 15)]) = qg[u];
+  }
+  __syncthreads();
+  // Q^T operands: [query tile qq][k-step]: query 16 qq + li, dims 32 s + 8j .. +8
+  u32x4 qf[2][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      qf[qq][st] = *reinterpret_cast<const u32x4*>(&qs[(16 * qq + li) * QS_LD + 8 * j + 32 * st]);
 
   f32x4 oacc[2][8];
 #pragma unroll
@@ -150,8 +170,7 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
         p[e] = x;
         mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      mx = xor32_combine(xor16_combine(mx, fmax_op), fmax_op);
       const float m_new = fmaxf(m_run[qq], mx);
       // a sub-tile with no valid key at all leaves the state unchanged
       const float alpha = (m_new == -INFINITY || m_run[qq] == -INFINITY)
@@ -163,8 +182,7 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
         p[e] = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[e] - m_new);
         ls += p[e];
       }
-      ls += __shfl_xor(ls, 16, kWave);
-      ls += __shfl_xor(ls, 32, kWave);
+      ls = xor32_combine(xor16_combine(ls, add_op), add_op);
       l_run[qq] = l_run[qq] * alpha + ls;
       m_run[qq] = m_new;
       u16x8 pb;
@@ -180,12 +198,9 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
   };
 
   if constexpr (ONE) {
-    KVTile16 ta;
-    load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
     consume(ta, wkey0);
   } else {
-    KVTile16 ta, tb;
-    load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
+    KVTile16 tb;
     for (int n = 0; n < nsub; n += 2) {
       if (n + 1 < nsub) load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
       consume(ta, wkey0 + 32 * n);
@@ -391,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
         tmax = fmaxf(tmax, x);
       }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    tmax = xor32_combine(tmax, fmax_op);
     const float m_new = fmaxf(m_run, tmax);   // finite: every tile has a valid key
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     float ls = 0.f;
@@ -402,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
         p[st][v] = __builtin_amdgcn_exp2f(p[st][v] - m_new);
         ls += p[st][v];
       }
-    ls += __shfl_xor(ls, 32, kWave);
+    ls = xor32_combine(ls, add_op);
     l_run = l_run * alpha + ls;
     m_run = m_new;
 #pragma unroll
