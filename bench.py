@@ -271,6 +271,8 @@ def main():
                     help="also run plain device copies of this many MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counter scale)")
     ap.add_argument("--roofline-kernel", default="auto")
+    ap.add_argument("--profile-every", type=int, default=7,
+                    help="time one launch in N of the roofline kernel class")
     ap.add_argument("--logit-scale", type=float, default=0.0,
                     help="override the calibrated scale (exploration only)")
     a = ap.parse_args()
@@ -318,7 +320,9 @@ def main():
 
     cls = DOMINANT.get(wl.name, "REF_GATE_UP") if a.roofline_kernel == "auto" else a.roofline_kernel
     cid = bd.KERNEL_CLASSES.index(cls)
-    lib.call("dllm_profile_select", cid)
+    # time one launch in a.profile_every (7 is coprime with the layer counts, so the
+    # sample rotates through every layer); each timed launch costs two event records
+    lib.call("dllm_profile_select_every", cid, a.profile_every)
     stats = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -353,6 +357,7 @@ def main():
     roof["traffic"] = counters_for(cls, wl.name)
     roof["kernel"] = cls
     roof["launches"] = n_launch.value
+    roof["sampled_every"] = a.profile_every
     roof["avg_launch_us"] = round(avg_s * 1e6, 2)
 
     out = {

@@ -77,6 +77,7 @@ _SIGS = {
     "dllm_status_string": (C.c_char_p, [_I]),
     "dllm_last_error": (C.c_char_p, []),
     "dllm_profile_select": (_I, [_I]),
+    "dllm_profile_select_every": (_I, [_I, _I]),
     "dllm_profile_read": (_I, [C.POINTER(C.c_int32), C.POINTER(C.c_double)]),
     "dllm_synth_fill": (_I, [_P, C.c_int64, _I, C.c_uint64, C.c_uint32, C.c_double, _I, _P]),
 }

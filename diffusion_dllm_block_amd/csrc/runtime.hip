@@ -38,6 +38,8 @@ dllm_status fail(dllm_status st, const char* fmt, ...) {
 // ------------------------------------------------------------------ profiling
 struct Prof {
   int cls = DLLM_K_NONE;
+  int every = 1;               // time one launch in `every`
+  long long seen = 0;          // launches of the class since selection
   std::vector<hipEvent_t> ev;  // pairs
   size_t used = 0;             // events recorded
 };
@@ -48,10 +50,16 @@ struct ProfScope {
   bool on;
   ProfScope(int cls, hipStream_t s) : st(s), on(cls == g_prof.cls) {
     if (!on) return;
+    on = (g_prof.seen++ % g_prof.every) == 0;
+    if (!on) return;
     if (g_prof.used + 2 > g_prof.ev.size()) {
       for (int i = 0; i < 256; ++i) {
         hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) { on = false; return; }
+        // timing only: no system-scope fence (an L2 write-back and invalidate) at record
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
+          on = false;
+          return;
+        }
         g_prof.ev.push_back(e);
       }
     }
@@ -628,12 +636,19 @@ const char* dllm_status_string(dllm_status st) {
 
 const char* dllm_last_error(void) { return g_err.c_str(); }
 
-dllm_status dllm_profile_select(int32_t kernel_class) {
+dllm_status dllm_profile_select_every(int32_t kernel_class, int32_t every) {
   if (kernel_class < DLLM_K_NONE || kernel_class >= DLLM_K_COUNT)
     return fail(DLLM_E_ARG, "bad kernel class %d", kernel_class);
+  if (every < 1) return fail(DLLM_E_ARG, "bad sampling stride %d", every);
   g_prof.cls = kernel_class;
+  g_prof.every = every;
+  g_prof.seen = 0;
   g_prof.used = 0;
   return DLLM_OK;
+}
+
+dllm_status dllm_profile_select(int32_t kernel_class) {
+  return dllm_profile_select_every(kernel_class, 1);
 }
 
 dllm_status dllm_profile_read(int32_t* launches, double* total_ms) {

@@ -218,7 +218,10 @@ const char* dllm_status_string(dllm_status st);
 const char* dllm_last_error(void);
 
 /* Per-kernel-class timing with HIP events on the launching stream.  Select one class
- * (or -1 for none); every later launch of that class is bracketed by two events;
+ * (or -1 for none); every later launch of that class (with dllm_profile_select_every:
+ * one launch in `every`, counted over all launches of the class, so a stride coprime
+ * with the layer count visits every layer) is bracketed by two events (timing-only
+ * events without a system-scope fence);
  * dllm_profile_read() synchronises on the recorded events and returns the number of
  * launches and their summed duration, then clears the record.  A GEMM class times the
  * GEMM kernel alone; the split-K reduction that applies a step GEMM's epilogue (QKV,
@@ -232,6 +235,8 @@ typedef enum {
   DLLM_K_COUNT
 } dllm_kernel_class;
 dllm_status dllm_profile_select(int32_t kernel_class);
+/* As dllm_profile_select, sampling one launch in `every` (every >= 1; 1 = all).          */
+dllm_status dllm_profile_select_every(int32_t kernel_class, int32_t every);
 dllm_status dllm_profile_read(int32_t* launches, double* total_ms);
 
 #ifdef __cplusplus

@@ -141,3 +141,6 @@ def test_kernel_entry_validation(lib):
     assert h(FAKE, FAKE, FAKE, 4, 4, 256, bd.BF16, 3, 1.0, None, 0, None) == -7
     assert h(FAKE, FAKE, FAKE, 4, 4, 384, bd.BF16, 0, 1.0, None, 0, None) == -3
     assert lib.cdll.dllm_profile_select(99) == -7
+    assert lib.cdll.dllm_profile_select_every(99, 1) == -7
+    assert lib.cdll.dllm_profile_select_every(0, 0) == -7
+    assert lib.cdll.dllm_profile_select_every(-1, 7) == 0
