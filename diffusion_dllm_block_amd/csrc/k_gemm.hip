@@ -608,6 +608,19 @@ __device__ __forceinline__ float4 sum_split4(const PartView& pv, int m, int c) {
   return s;
 }
 
+// Deferred RMS factor of row m (1 when the input was already normalised); the segment
+// sums are added in segment order.
+__device__ __forceinline__ float row_rms_factor(const EpiArgs& e, int m) {
+  if (e.rss == nullptr) return 1.f;
+  const float* s = e.rss + (int64_t)m * e.rseg;
+  float t = 0.f;
+  for (int i = 0; i < e.rseg; ++i) t += s[i];
+  return 1.0f / sqrtf(t / (float)e.rd + e.reps);
+}
+__device__ __forceinline__ float4 scale4(float4 v, float r) {
+  return make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+}
+
 template <int EPI>
 __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
   const int M = pv.M, Nv = pv.N;
@@ -616,7 +629,7 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     // Nv % 4 == 0: 4 outputs of one row
     if (i4 >= (int64_t)M * Nv) return;
     const int m = (int)(i4 / Nv), vc = (int)(i4 % Nv);
-    float4 v = sum_split4(pv, m, vc);
+    const float4 v = scale4(sum_split4(pv, m, vc), row_rms_factor(e, m));
     if constexpr (EPI == EPI_F32) {
       float4 o = make_float4(v.x * e.scale, v.y * e.scale, v.z * e.scale, v.w * e.scale);
       *reinterpret_cast<float4*>((float*)e.y + (int64_t)m * e.ldy + vc) = o;
@@ -629,8 +642,9 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     if (i4 >= (int64_t)M * e.F) return;
     const int m = (int)(i4 / e.F), c = (int)(i4 % e.F);
     const int vg = 64 * (c >> 5) + (c & 31);
-    float4 gt = sum_split4(pv, m, vg);
-    float4 up = sum_split4(pv, m, vg + 32);
+    const float r = row_rms_factor(e, m);
+    const float4 gt = scale4(sum_split4(pv, m, vg), r);
+    const float4 up = scale4(sum_split4(pv, m, vg + 32), r);
     uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.F + c;
     y[0] = f2bf(silu(gt.x) * up.x); y[1] = f2bf(silu(gt.y) * up.y);
     y[2] = f2bf(silu(gt.z) * up.z); y[3] = f2bf(silu(gt.w) * up.w);
@@ -642,8 +656,9 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     const int rem = (int)(i4 % (nslot * 64));
     const int hs = rem / 64, d = rem % 64;
     const int vc = 64 * (2 * hs + (d >> 5)) + (d & 31);
-    float4 a = sum_split4(pv, m, vc);
-    float4 b = sum_split4(pv, m, vc + 32);
+    const float r = row_rms_factor(e, m);
+    const float4 a = scale4(sum_split4(pv, m, vc), r);
+    const float4 b = scale4(sum_split4(pv, m, vc + 32), r);
     const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
     float x1[4] = {a.x, a.y, a.z, a.w}, x2[4] = {b.x, b.y, b.z, b.w};
     if (hs < e.Hq + e.Hkv) {
@@ -696,7 +711,7 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     p.kchunk = K;
     return p;
   }
-  if (M <= 64) {
+  if (M <= kSkinnyRows) {
     p.kind = GEMM_SKINNY;
     p.mt = (M <= 16) ? 1 : (M <= 32) ? 2 : 4;
     p.ntn = (Nv + 15) / 16;  // 16-column groups

@@ -265,6 +265,75 @@ hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, cons
   return hipGetLastError();
 }
 
+template <typename T>
+__global__ __launch_bounds__(kFoldSeg / 4) void fold_scale_kernel(float* x, int Rin, int Kout,
+                                                                 const T* g, int d, T* h,
+                                                                 float* rss, PartView pv) {
+  constexpr int NW = kFoldSeg / 4 / kWave;
+  __shared__ float red[NW];
+  const int j = blockIdx.y, seg = blockIdx.x;
+  const int in_row = (j / Kout) * Rin + (j % Kout);
+  const int col = seg * kFoldSeg + 4 * (int)threadIdx.x;
+  const bool ok = col < d;
+  const int c = ok ? col : 0;  // clamped, never stored
+  float* xr = x + (int64_t)in_row * d;
+  float4 v = *reinterpret_cast<const float4*>(xr + c);
+  float gv[4];
+  if constexpr (sizeof(T) == 2) {
+    const u16x4 gg = *reinterpret_cast<const u16x4*>(g + c);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) gv[u] = bf2f(gg[u]);
+  } else {
+    const float4 gg = *reinterpret_cast<const float4*>(g + c);
+    gv[0] = gg.x; gv[1] = gg.y; gv[2] = gg.z; gv[3] = gg.w;
+  }
+  const int64_t stride = pv.split_stride();
+  for (int s0 = 0; s0 < pv.splits; s0 += 8) {  // all of a group's loads in flight together
+    float4 pp[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      pp[u] = *reinterpret_cast<const float4*>(pv.p + min(s0 + u, pv.splits - 1) * stride +
+                                               pv.off(in_row, c));
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < pv.splits) { v.x += pp[u].x; v.y += pp[u].y; v.z += pp[u].z; v.w += pp[u].w; }
+  }
+  if (ok) {
+    if (pv.splits > 0) *reinterpret_cast<float4*>(xr + c) = v;
+    const float o0 = v.x * gv[0], o1 = v.y * gv[1], o2 = v.z * gv[2], o3 = v.w * gv[3];
+    T* hr = h + (int64_t)j * d + c;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<u16x4*>(hr) = u16x4{f2bf(o0), f2bf(o1), f2bf(o2), f2bf(o3)};
+    } else {
+      *reinterpret_cast<float4*>(hr) = make_float4(o0, o1, o2, o3);
+    }
+  }
+  float q = ok ? v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w : 0.f;
+  q = wave_sum_dpp(q);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = q;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) t += red[i];
+    rss[(int64_t)j * gridDim.x + seg] = t;
+  }
+}
+
+hipError_t launch_fold_scale(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
+                             int d, void* h, float* rss, const PartView& pv, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 4) return hipErrorInvalidValue;
+  const dim3 grid((d + kFoldSeg - 1) / kFoldSeg, rows);
+  if (dtype == F32)
+    fold_scale_kernel<float><<<grid, kFoldSeg / 4, 0, st>>>(x, Rin, Kout, (const float*)g, d,
+                                                           (float*)h, rss, pv);
+  else
+    fold_scale_kernel<uint16_t><<<grid, kFoldSeg / 4, 0, st>>>(x, Rin, Kout, (const uint16_t*)g, d,
+                                                              (uint16_t*)h, rss, pv);
+  return hipGetLastError();
+}
+
 __global__ void fold_partials_kernel(float* y, PartView pv) {
   const int64_t n = (int64_t)pv.M * pv.N;
   const int64_t stride = pv.split_stride();

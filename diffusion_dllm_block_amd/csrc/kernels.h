@@ -31,9 +31,16 @@ struct EpiArgs {
   const float* rcos = nullptr;     // [S][D/2]
   const float* rsin = nullptr;
   int Hq = 0, Hkv = 0, D = 0, R = 0, pos0 = 0, Sp = 0;
+  // Deferred RMS factor (skinny split-K reduction only): when rss is set, the GEMM input
+  // was bf16(x * g) and row m of the result is multiplied by
+  // 1 / sqrt(sum(rss[m][0..rseg)) / rd + reps) before the epilogue.
+  const float* rss = nullptr;
+  int rseg = 0, rd = 0;
+  float reps = 0.f;
 };
 
 enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3 };
+constexpr int kSkinnyRows = 64;  // bf16 GEMMs with at most this many rows stream weights
 
 // Where split-K partial sums live.  Plain: [split][M][N].  Blocked (skinny GEMM): per split,
 // per 16-column group, one block of mrows x 16 floats in which row m, column c sits at
@@ -118,6 +125,13 @@ hipError_t launch_embed_norm(int dtype, const int* tokens, int S, int r0, int R,
 // order), written back into x.
 hipError_t launch_rmsnorm(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
                           float eps, int d, void* h, const PartView& pv, hipStream_t st);
+// RMSNorm with the row factor deferred to the consumer: for j < rows, x[in_row(j)] += the
+// pending split partials (split order), h[j] = x[in_row(j)] * g (no 1/rms), and
+// rss[j][s] = the sum of squares of columns [s*kFoldSeg, (s+1)*kFoldSeg) of that row.
+// grid (ceil(d / kFoldSeg), rows): every CU takes a share of the rows.
+constexpr int kFoldSeg = 512;
+hipError_t launch_fold_scale(int dtype, float* x, int rows, int Rin, int Kout, const void* g,
+                             int d, void* h, float* rss, const PartView& pv, hipStream_t st);
 // y[m][c] += sum over splits of the partials at (m, c), in split order (y is [M][N] fp32)
 hipError_t launch_fold_partials(float* y, const PartView& pv, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st);

@@ -146,7 +146,7 @@ int step_rows(const Dims& d, int b) {
 
 struct Ws {
   size_t x, h, q, o, a, logits, rcos, rsin, gpart, gcnt, apart, acnt, cpm, cps, cpi,
-      conf, argmax, nun, rem, total;
+      conf, argmax, nun, rem, rss, total;
   size_t gpart_floats, apart_floats;
   int gcnt_n, acnt_n;
 };
@@ -198,6 +198,8 @@ Ws plan_ws(const Dims& d) {
   w.argmax = take((size_t)d.B * d.K * 4);
   w.nun = take((size_t)d.B * 4);
   w.rem = take((size_t)d.B * 4);
+  // per-row segment sums of squares of a deferred-factor RMSNorm (rows <= kSkinnyRows)
+  w.rss = take((size_t)kSkinnyRows * ((d.d + kFoldSeg - 1) / kFoldSeg) * 4);
   // counters last, contiguous, zeroed at prefill
   w.gcnt = take((size_t)gcn * 4);
   w.acnt = take((size_t)acn * 4);
@@ -231,6 +233,13 @@ struct Pending {  // split-K partials of a residual GEMM not yet added into x
   PartView view;
 };
 
+// The RMS factor of the last norm, left for the next GEMM's split-K reduction to apply.
+struct RowScale {
+  bool on = false;
+  const float* rss = nullptr;
+  int rseg = 0;
+};
+
 struct Ctx {
   const Dims& d;
   const dllm_model_desc* m;
@@ -239,6 +248,7 @@ struct Ctx {
   char* ws;
   hipStream_t st;
   mutable Pending pend;
+  mutable RowScale rs;
   template <typename P> P* at(size_t off) const { return reinterpret_cast<P*>(ws + off); }
   void* cache_k(int l) const {
     return (char*)s->kv_cache + (size_t)l * 2 * d.B * d.Hkv * d.Sp * d.D * d.esz;
@@ -255,14 +265,24 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
     return fail(DLLM_E_WORKSPACE, "internal: GEMM plan exceeds the workspace plan");
   if (c.pend.splits)
     return fail(DLLM_E_STATE, "internal: pending residual partials not consumed");
+  EpiArgs er = e;
+  if (c.rs.on) {  // the input rows still carry their RMS factor
+    if (p.kind != GEMM_SKINNY || epi == EPI_RESID)
+      return fail(DLLM_E_STATE, "internal: deferred RMS factor without a split-K reduction");
+    er.rss = c.rs.rss;
+    er.rseg = c.rs.rseg;
+    er.rd = c.d.d;
+    er.reps = c.d.eps;
+    c.rs = RowScale{};
+  }
   {
     ProfScope ps(cls, c.st);
-    HIP_TRY(launch_gemm_only(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, e, c.at<float>(c.w.gpart),
+    HIP_TRY(launch_gemm_only(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, er, c.at<float>(c.w.gpart),
                              c.at<int>(c.w.gcnt), c.st));
   }
   if (p.kind == GEMM_SKINNY && epi != EPI_RESID) {
     ProfScope ps(DLLM_K_SPLIT_REDUCE, c.st);
-    HIP_TRY(launch_reduce_epilogue(epi, p.view(c.at<float>(c.w.gpart), M, Nv), e, c.st));
+    HIP_TRY(launch_reduce_epilogue(epi, p.view(c.at<float>(c.w.gpart), M, Nv), er, c.st));
   }
   if (p.deferred && epi == EPI_RESID) {
     c.pend.splits = p.splits;
@@ -272,12 +292,24 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
 }
 
 // RMSNorm of `rows` rows of x into h (see launch_rmsnorm); adds pending residual partials.
+// When the consumer is a skinny bf16 GEMM (rows <= kSkinnyRows) the per-row factor is
+// deferred: h = x * g, spread over (row, 512-column segment) workgroups, and the GEMM's
+// split-K reduction multiplies each row by 1 / rms (it distributes over the row's dot
+// products), so no kernel needs a whole row on one CU.
 dllm_status norm(const Ctx& c, int rows, int Rin, int Kout, const void* g) {
   ProfScope ps(DLLM_K_RMSNORM, c.st);
   PartView pv = c.pend.view;
   pv.splits = c.pend.splits;
-  HIP_TRY(launch_rmsnorm(c.d.dtype, c.at<float>(c.w.x), rows, Rin, Kout, g, c.d.eps, c.d.d,
-                         c.at<void>(c.w.h), pv, c.st));
+  if (c.d.dtype == BF16 && rows <= kSkinnyRows) {
+    HIP_TRY(launch_fold_scale(c.d.dtype, c.at<float>(c.w.x), rows, Rin, Kout, g, c.d.d,
+                              c.at<void>(c.w.h), c.at<float>(c.w.rss), pv, c.st));
+    c.rs.on = true;
+    c.rs.rss = c.at<float>(c.w.rss);
+    c.rs.rseg = (c.d.d + kFoldSeg - 1) / kFoldSeg;
+  } else {
+    HIP_TRY(launch_rmsnorm(c.d.dtype, c.at<float>(c.w.x), rows, Rin, Kout, g, c.d.eps, c.d.d,
+                           c.at<void>(c.w.h), pv, c.st));
+  }
   c.pend = Pending{};
   return DLLM_OK;
 }
@@ -341,6 +373,7 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
 dllm_status do_refresh(const Ctx& c) {
   dllm_status st = run_layers(c, 0, c.d.S, true);
   c.pend = Pending{};  // the last layer's tail is skipped: nothing is pending
+  c.rs = RowScale{};
   return st;
 }
 
