@@ -66,6 +66,8 @@ _SIGS = {
     "dllm_prefill_cache": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _P]),
     "dllm_refresh_cache": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P]),
     "dllm_block_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P, _P]),
+    "dllm_refresh_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P,
+                               _P]),
     "dllm_generate": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _P, C.POINTER(Stats)]),
     "dllm_kernel_workspace_bytes": (C.c_size_t, [_I] * 7),
     "dllm_kernel_block_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,

@@ -314,8 +314,9 @@ dllm_status norm(const Ctx& c, int rows, int Rin, int Kout, const void* g) {
   return DLLM_OK;
 }
 
-// Layer stack over R rows per sequence starting at absolute position r0.
-dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
+// Layer stack over R rows per sequence starting at absolute position r0, from layer l0
+// (l0 > 0: x already holds the input of layer l0 in rows [0, B*R)).
+dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh, int l0 = 0) {
   const Dims& d = c.d;
   const int M = d.B * R;
   float* x = c.at<float>(c.w.x);
@@ -323,7 +324,7 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
   void* q = c.at<void>(c.w.q);
   void* o = c.at<void>(c.w.o);
   void* a = c.at<void>(c.w.a);
-  {
+  if (l0 == 0) {
     ProfScope ps(DLLM_K_EMBED_NORM, c.st);
     HIP_TRY(launch_embed_norm(d.dtype, c.s->tokens, d.S, r0, R, d.B, c.m->embed,
                               c.m->attn_norm[0], d.eps, d.d, d.V, x, h, c.st));
@@ -332,7 +333,7 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh) {
   if (ap.part_floats > c.w.apart_floats || ap.counters > c.w.acnt_n)
     return fail(DLLM_E_WORKSPACE, "internal: attention plan exceeds the workspace plan");
   const int Nqkv = (d.Hq + 2 * d.Hkv) * d.D;
-  for (int l = 0; l < d.L; ++l) {
+  for (int l = l0; l < d.L; ++l) {
     if (l > 0) {
       dllm_status st = norm(c, M, R, R, c.m->attn_norm[l]);
       if (st) return st;
@@ -385,16 +386,15 @@ dllm_status do_init(const Ctx& c) {
   return DLLM_OK;
 }
 
-dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, float* conf,
-                    int* argmax) {
+// Final norm over the block rows (the first K of each sequence's R computed rows), LM
+// head, confidence and threshold unmask.
+dllm_status decode_tail(const Ctx& c, int b, int R, int* n_un, int* rem, float* logits,
+                        float* conf, int* argmax) {
   const Dims& d = c.d;
   const int s0 = d.P + b * d.K;
-  const int R = step_rows(d, b);
-  dllm_status st = run_layers(c, s0, R, false);
+  dllm_status st = norm(c, d.B * d.K, R, d.K, c.m->final_norm);
   if (st) return st;
   void* h = c.at<void>(c.w.h);
-  st = norm(c, d.B * d.K, R, d.K, c.m->final_norm);
-  if (st) return st;
   float* lg = logits ? logits : c.at<float>(c.w.logits);
   EpiArgs el;
   el.y = lg; el.ldy = d.V; el.scale = d.lscale;
@@ -408,6 +408,46 @@ dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, flo
                              c.at<float>(c.w.cpm), c.at<float>(c.w.cps), c.at<int>(c.w.cpi),
                              c.st));
   return DLLM_OK;
+}
+
+dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, float* conf,
+                    int* argmax) {
+  const Dims& d = c.d;
+  const int R = step_rows(d, b);
+  dllm_status st = run_layers(c, d.P + b * d.K, R, false);
+  if (st) return st;
+  return decode_tail(c, b, R, n_un, rem, logits, conf, argmax);
+}
+
+// Staging room for the block rows of x: the FFN activation buffer, idle between layers.
+bool refresh_step_fits(const Dims& d) {
+  return (size_t)d.B * d.S * d.F * d.esz >= (size_t)d.B * d.K * d.d * sizeof(float);
+}
+
+// The block's first denoising step fused with its refresh (by property (a) the first
+// step after a refresh equals the full forward): the full forward over all S rows
+// writes every layer's K/V and leaves the last layer's input in x; the block rows of x
+// move to the cached-step row layout, and only the last layer, over the block rows
+// (attending to all S fresh keys), the final norm, LM head and unmask follow.  Saves
+// the block-row recompute of layers 0 .. L-2 that a separate first step would do.
+dllm_status do_refresh_step(const Ctx& c, int b, int* n_un, int* rem, float* logits,
+                            float* conf, int* argmax) {
+  const Dims& d = c.d;
+  dllm_status st = (b == 0) ? do_init(c) : DLLM_OK;
+  if (st) return st;
+  st = do_refresh(c);
+  if (st) return st;
+  if (!refresh_step_fits(d)) return do_step(c, b, n_un, rem, logits, conf, argmax);
+  const int s0 = d.P + b * d.K;
+  const size_t row = (size_t)d.d * sizeof(float);
+  float* x = c.at<float>(c.w.x);
+  void* tmp = c.at<void>(c.w.a);
+  HIP_TRY(hipMemcpy2DAsync(tmp, d.K * row, x + (size_t)s0 * d.d, (size_t)d.S * row, d.K * row,
+                           d.B, hipMemcpyDeviceToDevice, c.st));
+  HIP_TRY(hipMemcpyAsync(x, tmp, (size_t)d.B * d.K * row, hipMemcpyDeviceToDevice, c.st));
+  st = run_layers(c, s0, d.K, false, d.L - 1);
+  if (st) return st;
+  return decode_tail(c, b, d.K, n_un, rem, logits, conf, argmax);
 }
 
 dllm_status setup(const dllm_model_desc* m, const dllm_seq_desc* s, Dims* d, Ws* w) {
@@ -475,6 +515,19 @@ dllm_status dllm_block_step(const dllm_model_desc* m, const dllm_seq_desc* s, in
   return do_step(c, block, d_n_unmasked, d_remaining, d_logits, d_conf, d_argmax);
 }
 
+dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
+                              dllm_stream_t stream, int32_t* d_n_unmasked, int32_t* d_remaining,
+                              float* d_logits, float* d_conf, int32_t* d_argmax) {
+  Dims d;
+  Ws w;
+  dllm_status st = setup(m, s, &d, &w);
+  if (st) return st;
+  if (block < 0 || block >= d.nblocks) return fail(DLLM_E_STATE, "block %d outside [0, %d)", block, d.nblocks);
+  if (!d_n_unmasked || !d_remaining) return fail(DLLM_E_NULL, "n_unmasked/remaining is NULL");
+  Ctx c{d, m, s, w, (char*)s->workspace, (hipStream_t)stream};
+  return do_refresh_step(c, block, d_n_unmasked, d_remaining, d_logits, d_conf, d_argmax);
+}
+
 dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm_stream_t stream,
                           dllm_stats* out) {
   Dims d;
@@ -483,29 +536,24 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
   if (st) return st;
   hipStream_t hs = (hipStream_t)stream;
   Ctx c{d, m, s, w, (char*)s->workspace, hs};
-  int32_t* host = nullptr;  // pinned: [B] remaining + [B*K] block tokens
-  HIP_TRY(hipHostMalloc((void**)&host, sizeof(int32_t) * (d.B + d.B * d.K), hipHostMallocDefault));
+  int32_t* host = nullptr;  // pinned: [B] remaining
+  HIP_TRY(hipHostMalloc((void**)&host, sizeof(int32_t) * d.B, hipHostMallocDefault));
   struct Free { int32_t* p; ~Free() { if (p) (void)hipHostFree(p); } } guard{host};
   const double t_start = now_ms();
   double ms_ref = 0, ms_step = 0;
   int steps = 0, refreshes = 0;
   for (int b = 0; b < d.nblocks; ++b) {
+    // refresh (prefill for block 0) fused with the block's first step
     double t0 = now_ms();
-    st = (b == 0) ? do_init(c) : DLLM_OK;
-    if (st) return st;
-    st = do_refresh(c);
+    st = do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
     if (st) return st;
     ++refreshes;
-    // does the block still hold mask tokens?
-    const int s0 = d.P + b * d.K;
-    HIP_TRY(hipMemcpy2DAsync(host + d.B, d.K * sizeof(int32_t), s->tokens + s0,
-                             (size_t)d.S * sizeof(int32_t), d.K * sizeof(int32_t), d.B,
-                             hipMemcpyDeviceToHost, hs));
+    HIP_TRY(hipMemcpyAsync(host, c.at<int>(w.rem), d.B * sizeof(int32_t), hipMemcpyDeviceToHost, hs));
     HIP_TRY(hipStreamSynchronize(hs));
     ms_ref += now_ms() - t0;
     bool any = false;
-    for (int i = 0; i < d.B * d.K; ++i) any |= host[d.B + i] == d.mask;
-    int n = 0;
+    for (int i = 0; i < d.B; ++i) any |= host[i] != 0;
+    int n = 1;
     t0 = now_ms();
     while (any) {
       st = do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);

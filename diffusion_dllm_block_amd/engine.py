@@ -128,6 +128,15 @@ class Session:
         self.lib.call("dllm_refresh_cache", *self._args(), block, bd.stream_handle(stream))
 
     def step(self, block: int, logits: bool = True, stream=None) -> dict:
+        """One cached denoising step of `block` (dllm_block_step)."""
+        return self._decode("dllm_block_step", block, logits, stream)
+
+    def refresh_step(self, block: int, logits: bool = True, stream=None) -> dict:
+        """The refresh of `block` (the prefill for block 0) fused with its first step
+        (dllm_refresh_step)."""
+        return self._decode("dllm_refresh_step", block, logits, stream)
+
+    def _decode(self, entry: str, block: int, logits: bool, stream) -> dict:
         torch = _torch()
         dev = self.tokens.device
         out = {"n_unmasked": self.n_unmasked, "remaining": self.remaining}
@@ -135,7 +144,7 @@ class Session:
                          device=dev) if logits else None
         conf = torch.empty((self.B, self.K), dtype=torch.float32, device=dev)
         arg = torch.empty((self.B, self.K), dtype=torch.int32, device=dev)
-        self.lib.call("dllm_block_step", *self._args(), block, bd.stream_handle(stream),
+        self.lib.call(entry, *self._args(), block, bd.stream_handle(stream),
                       bd.ptr(self.n_unmasked), bd.ptr(self.remaining), bd.ptr(lg), bd.ptr(conf),
                       bd.ptr(arg))
         out.update(logits=lg, conf=conf, argmax=arg)

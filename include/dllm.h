@@ -121,7 +121,8 @@ typedef struct {
 } dllm_seq_desc;
 
 typedef struct {
-  int32_t steps;                      /* cached denoising steps run                      */
+  int32_t steps;                      /* denoising steps run (each block's first one
+                                         fused with its refresh)                         */
   int32_t refreshes;                  /* full forwards run (prefill included)            */
   int32_t tokens;                     /* tokens generated (batch * gen_len)              */
   int32_t blocks;
@@ -160,9 +161,21 @@ dllm_status dllm_block_step(const dllm_model_desc* m, const dllm_seq_desc* s, in
                             dllm_stream_t stream, int32_t* d_n_unmasked, int32_t* d_remaining,
                             float* d_logits, float* d_conf, int32_t* d_argmax);
 
-/* Whole generation: prefill, then for every block cached steps until the block has no
- * mask token left (one 4*batch-byte device-to-host read per step), then a refresh
- * (not after the last block).  Synchronous.  `out` may be NULL.                     */
+/* A block's refresh fused with its first denoising step.  By [A] property (a) the first
+ * step after a refresh equals the full forward, so the full forward over all S
+ * positions (K/V of every layer rewritten in place; for block 0 this is the prefill
+ * and also initialises the workspace, as dllm_prefill_cache does) is followed only by
+ * the last layer over the block rows [s0, s1) against all S fresh keys, the final
+ * norm, LM head, confidence and unmask.  Outputs as for dllm_block_step; the result
+ * equals dllm_refresh_cache (or dllm_prefill_cache) then dllm_block_step up to
+ * floating-point rounding order.                                                     */
+dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
+                              dllm_stream_t stream, int32_t* d_n_unmasked, int32_t* d_remaining,
+                              float* d_logits, float* d_conf, int32_t* d_argmax);
+
+/* Whole generation: for every block, dllm_refresh_step (the prefill for block 0), then
+ * cached steps until the block has no mask token left (one 4*batch-byte device-to-host
+ * read per step).  Synchronous.  `out` may be NULL.                                  */
 dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s,
                           dllm_stream_t stream, dllm_stats* out);
 

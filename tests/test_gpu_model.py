@@ -159,6 +159,54 @@ def test_first_step_after_refresh_matches_full_forward_bf16(lib):
         assert rel_inf(got, ref) < 2e-2
 
 
+@pytest.mark.parametrize("kind,mode", [("fp32", "dual"), ("fp32", "prefix"), ("bf16", "dual"),
+                                       ("bf16", "prefix"), ("bf16_large_tiles", "dual")])
+def test_refresh_step_matches_full_forward(lib, kind, mode):
+    """dllm_refresh_step (a block's refresh fused with its first step) against the
+    oracle's no-cache full forward of the same tokens, property (a), for block 0 (the
+    prefill) and block 1; its unmask decisions wherever they cannot flip."""
+    if kind == "fp32":
+        wl, tol = replace(synth.WORKLOADS["tiny_dual"], cache_mode=mode), 1e-4
+    else:
+        wl, tol = small_bf16(mode=mode, P=400 if kind == "bf16_large_tiles" else 40), 2e-2
+    m = wl.model
+    M = om.OracleModel(wl)
+    prompt = synth.make_prompt(wl)
+    gs = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, wl.threshold, mode)
+    r = np.random.default_rng(11)
+    toks = np.concatenate([prompt, np.full((wl.batch, wl.gen_len), m.mask_id)], 1)
+    K = wl.block_len
+    for b in (0, 1):
+        s0 = wl.prompt_len + b * K
+        if b == 1:  # block 0 decoded (ids below mask_id = vocab - 1), some of block 1 too
+            toks[:, s0 - K:s0] = r.integers(0, m.mask_id, (wl.batch, K))
+            toks[:, s0:s0 + K // 4] = r.integers(0, m.mask_id, (wl.batch, K // 4))
+        gs.tokens.copy_(torch.from_numpy(toks.astype(np.int32)))
+        out = gs.refresh_step(b)
+        torch.cuda.synchronize()
+        _, ref = om.full_forward(M, toks, logit_rows=slice(s0, s0 + K))
+        got = out["logits"].cpu().numpy().reshape(ref.shape).astype(np.float64)
+        assert rel_inf(got, ref) < tol, f"block {b}"
+        conf, arg = decode.confidence_argmax(ref.reshape(-1, m.vocab), m.mask_id)
+        conf, arg = conf.reshape(wl.batch, K), arg.reshape(wl.batch, K)
+        blk = toks[:, s0:s0 + K]
+        want, U, wn, wr = decode.unmask(blk, conf, arg, m.mask_id, wl.threshold)
+        dl = np.max(np.abs(got - ref), axis=-1)
+        unc = conf * np.expm1(2.0 * dl) + 1e-6
+        ok = safe_sequences(conf, unc, wl.threshold, blk == m.mask_id)
+        gtok = gs.tokens.cpu().numpy()[:, s0:s0 + K]
+        gchanged = gtok != blk
+        for bb in np.nonzero(ok)[0]:
+            assert np.array_equal(gchanged[bb], U[bb]), f"block {b} seq {bb}"
+            assert out["n_unmasked"][bb].item() == wn[bb]
+            assert out["remaining"][bb].item() == wr[bb]
+            for i in np.nonzero(U[bb])[0]:
+                z = np.sort(ref[bb, i][np.arange(m.vocab) != m.mask_id])
+                if z[-1] - z[-2] > 2.0 * dl[bb, i] + 1e-6:
+                    assert gtok[bb, i] == want[bb, i], f"block {b} seq {bb} row {i}"
+        toks = gs.tokens.cpu().numpy().astype(np.int64)
+
+
 def test_generate_properties_llada_shape_two_blocks(lib):
     """The 8B LLaDA shape (weights made on the device), DualCache, 2 blocks of 32:
     every step decodes >= 1 token, blocks finish in <= 32 steps, no mask token is
