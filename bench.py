@@ -256,6 +256,41 @@ def kernel_only(lib, torch, bd, rounds: int = 10):
     return out
 
 
+def ablation(model, wl, torch):
+    """The two halves of the method switched on one at a time, on the same model and
+    prompts: no cache (every step a full forward) or the workload's cache, and one token
+    per step (threshold 2 > 1: only the forced pick) or threshold decoding.  One timed
+    generation each after a warm-up of the cached configuration."""
+    from diffusion_dllm_block_amd.engine import Session
+    prompt = synth.make_prompt(wl)
+    runs = [("no cache, one token per step", "none", 2.0),
+            ("no cache, parallel decoding", "none", wl.threshold),
+            (f"{wl.cache_mode} cache, one token per step", wl.cache_mode, 2.0),
+            (f"{wl.cache_mode} cache, parallel decoding (Fast-dLLM)", wl.cache_mode, wl.threshold)]
+    warm = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+    warm.generate()
+    del warm
+    out = []
+    for name, mode, tau in runs:
+        sess = Session(model, prompt, wl.gen_len, wl.block_len, tau, mode)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        _, st = sess.generate()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        out.append({"config": name, "cache": mode, "threshold": tau,
+                    "tokens_per_s": round(wl.batch * wl.gen_len / dt, 2),
+                    "seconds": round(dt, 3), "steps": st["steps"],
+                    "full_forwards": st["refreshes"],
+                    "tokens_per_step": round(wl.batch * wl.gen_len / st["steps"], 3)})
+        log(f"ablation {name}: {dt:.2f} s, {st['steps']} steps, {st['refreshes']} full forwards")
+        del sess
+    base = out[0]["seconds"]
+    for r in out:
+        r["speedup_vs_no_cache_one_token"] = round(base / r["seconds"], 2)
+    return {"workload": wl.name, "runs": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +300,8 @@ def main():
     ap.add_argument("--gen-len", type=int, default=0, help="override (for quick runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the kernel-only rates")
+    ap.add_argument("--ablation", action="store_true",
+                    help="cache on/off x parallel decoding on/off on the workload, one JSON line")
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the kernel-only rates (no generation; for profiling)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -312,6 +349,10 @@ def main():
                    wl.cache_mode)
     torch.cuda.synchronize()
     log(f"weights + buffers ready in {time.time() - t:.1f} s")
+    if a.ablation:
+        del sess
+        print(json.dumps({"ablation": ablation(model, wl, torch)}), flush=True)
+        return
 
     for i in range(a.warmup):
         sess.reset_tokens()

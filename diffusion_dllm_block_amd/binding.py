@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libdllm.so")
 HEADERS = [os.path.join(ROOT, "include", "dllm.h"), os.path.join(ROOT, "include", "dllm_synth.h")]
 
 F32, BF16 = 0, 1
-CACHE_PREFIX, CACHE_DUAL = 1, 2
+CACHE_NONE, CACHE_PREFIX, CACHE_DUAL = 0, 1, 2
 
 STATUS = {0: "DLLM_OK", -1: "DLLM_E_NULL", -2: "DLLM_E_SHAPE", -3: "DLLM_E_UNSUPPORTED",
           -4: "DLLM_E_WORKSPACE", -5: "DLLM_E_HIP", -6: "DLLM_E_STATE", -7: "DLLM_E_ARG"}

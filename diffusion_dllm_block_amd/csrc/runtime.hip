@@ -121,7 +121,8 @@ dllm_status dims_of(const dllm_model_desc* m, const dllm_seq_desc* s, Dims* o) {
     return fail(DLLM_E_SHAPE, "batch, gen_len, block_len must be >= 1 and prompt_len >= 0");
   if (s->gen_len % s->block_len) return fail(DLLM_E_SHAPE, "gen_len %% block_len != 0");
   if (s->block_len > 64) return fail(DLLM_E_UNSUPPORTED, "block_len > 64");
-  if (s->cache_mode != DLLM_CACHE_PREFIX && s->cache_mode != DLLM_CACHE_DUAL)
+  if (s->cache_mode != DLLM_CACHE_NONE && s->cache_mode != DLLM_CACHE_PREFIX &&
+      s->cache_mode != DLLM_CACHE_DUAL)
     return fail(DLLM_E_ARG, "bad cache_mode %d", s->cache_mode);
   if (std::isnan(s->threshold)) return fail(DLLM_E_ARG, "threshold is NaN");
   Dims& d = *o;
@@ -135,13 +136,16 @@ dllm_status dims_of(const dllm_model_desc* m, const dllm_seq_desc* s, Dims* o) {
   if ((double)d.B * d.S > 1e8 || (double)d.S > 1e6) return fail(DLLM_E_UNSUPPORTED, "sequence too long");
   if (d.dtype == DLLM_F32 && d.S > 12000)
     return fail(DLLM_E_UNSUPPORTED, "fp32 models support S <= 12000");
+  // a no-cache step stages the block rows of x in the FFN activation buffer
+  if (d.mode == DLLM_CACHE_NONE && (size_t)d.S * d.F * d.esz < (size_t)d.K * d.d * sizeof(float))
+    return fail(DLLM_E_UNSUPPORTED, "no-cache mode needs S * d_ffn * esize >= 4 * block_len * d_model");
   return DLLM_OK;
 }
 
 // Rows per sequence recomputed by a step of block b.
 int step_rows(const Dims& d, int b) {
   int s0 = d.P + b * d.K;
-  return d.mode == DLLM_CACHE_DUAL ? d.K : d.S - s0;
+  return d.mode == DLLM_CACHE_PREFIX ? d.S - s0 : d.K;
 }
 
 struct Ws {
@@ -512,6 +516,8 @@ dllm_status dllm_block_step(const dllm_model_desc* m, const dllm_seq_desc* s, in
   if (block < 0 || block >= d.nblocks) return fail(DLLM_E_STATE, "block %d outside [0, %d)", block, d.nblocks);
   if (!d_n_unmasked || !d_remaining) return fail(DLLM_E_NULL, "n_unmasked/remaining is NULL");
   Ctx c{d, m, s, w, (char*)s->workspace, (hipStream_t)stream};
+  if (d.mode == DLLM_CACHE_NONE)
+    return do_refresh_step(c, block, d_n_unmasked, d_remaining, d_logits, d_conf, d_argmax);
   return do_step(c, block, d_n_unmasked, d_remaining, d_logits, d_conf, d_argmax);
 }
 
@@ -556,7 +562,9 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
     int n = 1;
     t0 = now_ms();
     while (any) {
-      st = do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+      st = (d.mode == DLLM_CACHE_NONE)
+               ? do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr)
+               : do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
       if (st) return st;
       HIP_TRY(hipMemcpyAsync(host, c.at<int>(w.rem), d.B * sizeof(int32_t), hipMemcpyDeviceToHost, hs));
       HIP_TRY(hipStreamSynchronize(hs));
@@ -567,6 +575,7 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
     }
     ms_step += now_ms() - t0;
     steps += n;
+    if (d.mode == DLLM_CACHE_NONE) refreshes += n - 1;  // every step was a full forward
     if (out && out->steps_per_block) out->steps_per_block[b] = n;
   }
   if (out) {

@@ -99,7 +99,10 @@ class Session:
         toks = torch.full((B, self.S), model.shape.mask_id, dtype=torch.int32)
         toks[:, :P] = prompt
         self.tokens = toks.to(device)
-        self.mode = bd.CACHE_DUAL if mode == "dual" else bd.CACHE_PREFIX
+        modes = {"dual": bd.CACHE_DUAL, "prefix": bd.CACHE_PREFIX, "none": bd.CACHE_NONE}
+        if mode not in modes:
+            raise ValueError(f"cache mode {mode!r} not in {sorted(modes)}")
+        self.mode = modes[mode]
         self.desc = bd.SeqDesc(batch=B, prompt_len=P, gen_len=gen_len, block_len=block_len,
                                cache_mode=self.mode, threshold=threshold,
                                tokens=self.tokens.data_ptr())

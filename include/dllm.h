@@ -74,7 +74,10 @@ typedef enum {
 } dllm_status;
 
 typedef enum { DLLM_F32 = 0, DLLM_BF16 = 1 } dllm_dtype;
-typedef enum { DLLM_CACHE_PREFIX = 1, DLLM_CACHE_DUAL = 2 } dllm_cache_mode;
+/* DLLM_CACHE_NONE: no approximate cache, the reference the cached modes approximate
+ * (every denoising step is a full forward over all S positions of the current tokens;
+ * the kv_cache buffer is still needed as the forward's K/V scratch).                 */
+typedef enum { DLLM_CACHE_NONE = 0, DLLM_CACHE_PREFIX = 1, DLLM_CACHE_DUAL = 2 } dllm_cache_mode;
 
 /* Model weights.  Shapes are row-major; "T" is float (DLLM_F32) or bf16 (DLLM_BF16).
  * Supported: head_dim divides 128 (and is even); n_heads % n_kv_heads == 0;
@@ -146,7 +149,8 @@ dllm_status dllm_prefill_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
 dllm_status dllm_refresh_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
                                int32_t block, dllm_stream_t stream);
 
-/* One cached denoising step of block `block` ([A] 1.1 and 1.2):
+/* One cached denoising step of block `block` ([A] 1.1 and 1.2; with DLLM_CACHE_NONE the
+ * step is the full forward of dllm_refresh_step):
  *   DualCache: the block rows [s0, s1) are recomputed through every layer and attend
  *   to all S cached keys (their own K/V written in place first); prefix mode: rows
  *   [s0, S) are recomputed and only [0, s0) comes from the cache.  Then the final
@@ -175,7 +179,8 @@ dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, 
 
 /* Whole generation: for every block, dllm_refresh_step (the prefill for block 0), then
  * cached steps until the block has no mask token left (one 4*batch-byte device-to-host
- * read per step).  Synchronous.  `out` may be NULL.                                  */
+ * read per step); with DLLM_CACHE_NONE every step is a dllm_refresh_step.
+ * Synchronous.  `out` may be NULL.                                                   */
 dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s,
                           dllm_stream_t stream, dllm_stats* out);
 

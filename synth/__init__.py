@@ -182,7 +182,7 @@ class Workload:
     prompt_len: int
     gen_len: int
     block_len: int
-    cache_mode: str               # "dual" or "prefix"
+    cache_mode: str               # "dual", "prefix" or "none" (no cache)
     threshold: float = 0.9
     model_seed: int = 1234
     prompt_seed: int = 5678

@@ -82,6 +82,7 @@ def test_sizes_of_valid_descriptors(lib):
     (dict(seq=dict(K=128, G=128)), -3),
     (dict(seq=dict(tau=math.nan)), -7),
     (dict(seq=dict(mode=5)), -7),
+    (dict(seq=dict(mode=-1)), -7),
     (dict(seq=dict(B=0)), -2),
     (dict(model=dict(n_kv_heads=3)), -2),
     (dict(model=dict(head_dim=24)), -3),

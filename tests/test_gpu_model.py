@@ -105,6 +105,41 @@ def test_tiny_fp32_free_running_generate(lib):
         assert gst["steps_per_block"] == ost["steps_per_block"]
 
 
+def test_tiny_fp32_no_cache_generate(lib):
+    """No-cache mode (every step a full forward) against the oracle's no-cache decoding,
+    with and without parallel decoding (tau 0.9, and tau > 1: one token per step)."""
+    for tau in (0.9, 1.5):
+        wl = replace(synth.WORKLOADS["tiny_dual"], cache_mode="none", threshold=tau)
+        m = wl.model
+        M = om.OracleModel(wl)
+        prompt = synth.make_prompt(wl)
+        osess = OSession(M, prompt, wl.gen_len, wl.block_len, tau, "dual")
+        margins, steps_per_block = [], []
+        for b in range(osess.n_blocks):
+            n = 0
+            while not osess.block_done(b):
+                s0, s1 = osess.block_span(b)
+                _, z = om.full_forward(M, osess.tokens, logit_rows=slice(s0, s1))
+                B, K, V = z.shape
+                conf, arg = decode.confidence_argmax(z.reshape(B * K, V), m.mask_id)
+                conf, arg = conf.reshape(B, K), arg.reshape(B, K)
+                masked = osess.tokens[:, s0:s1] == m.mask_id
+                margins.append(decision_margin_ok(conf, tau, masked)[0])
+                new, *_ = decode.unmask(osess.tokens[:, s0:s1], conf, arg, m.mask_id, tau)
+                osess.tokens[:, s0:s1] = new
+                n += 1
+            steps_per_block.append(n)
+        gs = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, tau, "none")
+        got, gst = gs.generate()
+        assert gst["steps"] == sum(gst["steps_per_block"])
+        assert gst["refreshes"] == gst["steps"]          # every step a full forward
+        if tau > 1:
+            assert gst["steps_per_block"] == [wl.block_len] * osess.n_blocks
+        if all(margins):
+            assert np.array_equal(got, osess.tokens[:, wl.prompt_len:])
+            assert gst["steps_per_block"] == steps_per_block
+
+
 def small_bf16(Hq=2, Hkv=2, mode="dual", B=2, P=40, G=64, K=32, V=2048, gain=0.1, scale=12.0):
     m = synth.ModelShape(n_layers=2, d_model=256, n_heads=Hq, n_kv_heads=Hkv, head_dim=128,
                          d_ffn=512, vocab=V, logit_scale=scale, dtype="bf16")
