@@ -101,10 +101,15 @@ def counters_for(cls: str, wl_name: str):
     return ent.get("bytes_per_launch")
 
 
+# The files the counted kernels (the GEMMs) are built from; a change to any of them
+# invalidates the stored counter values.
+COUNTED_SOURCES = ("k_gemm.hip", "kernels.h", "common.h")
+
+
 def source_sha() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "diffusion_dllm_block_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in COUNTED_SOURCES:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
