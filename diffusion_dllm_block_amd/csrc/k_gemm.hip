@@ -273,7 +273,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Bs = As + 2 * 128 * TB_LD;
   float* tile = reinterpret_cast<float*>(smem);
-  const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+  // row tiles fastest: the row tiles of one weight tile are dispatched together, so the
+  // weight tile streams from HBM once and the others find it in the Infinity Cache
+  const int tm = blockIdx.x, tn = blockIdx.y, split = blockIdx.z;
   const int m0 = tm * 128, vc0 = tn * 128;
   const int tid = threadIdx.x;
   const int w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, lr = l & 31, g = l >> 5;
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
     int m = m0 + r, vc = vc0 + c;
     if (m < M && vc < Nv) st_dev(&part[((int64_t)split * M + m) * Nv + vc], tile[r * TL + c]);
   }
-  if (!arrive_last(&counters[tm * gridDim.x + tn], splits, &flag)) return;
+  if (!arrive_last(&counters[tm * gridDim.y + tn], splits, &flag)) return;
   gather_partials(tile, TL, 128, m0, vc0, M, Nv, splits, part);
   __syncthreads();
   epilogue<uint16_t, EPI>(tile, TL, 128, m0, vc0, M, Nv, e);
@@ -738,7 +740,10 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   const int small_tiles = ((Nv + 127) / 128) * ((M + 127) / 128);
   const bool big_fills = (epi == EPI_RESID && big_tiles < 256) ||
                          1.15 * fill(big_tiles, 256) >= fill(small_tiles, 512);
-  if (M >= 512 && K % TB_K == 0 && big_fills) {
+  // 256 <= M < 512 (one row tile of 256): the large tile reads each weight tile once,
+  // while the 128-row tiles read it twice; worth it once it fills a round of CUs
+  const bool big_mid = M >= 256 && M < 512 && big_tiles >= 256;
+  if (K % TB_K == 0 && ((M >= 512 && big_fills) || big_mid)) {
     p.kind = GEMM_BIG;
     p.ntn = (Nv + BG_T - 1) / BG_T;
     p.ntm = (M + BG_T - 1) / BG_T;
@@ -763,7 +768,11 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   const int ks = TB_K, target = 512;
   const int tiles = p.ntn * p.ntm;
   int splits = 1;
-  if (tiles < target) {
+  // Residual partials are plain stores folded by the next norm; the other epilogues hand
+  // split partials over through coherent stores and an arrival counter, which costs more
+  // than the extra parallelism gains unless the tile count is small (measured at
+  // M = 256: 72 tiles of a 4608-wide QKV take 61 us unsplit, 74-88 us with 2-8 splits).
+  if (tiles < target && (epi == EPI_RESID || tiles < 64)) {
     splits = (target + tiles - 1) / tiles;
     int maxs = K / ks;
     if (splits > maxs) splits = maxs;
@@ -843,7 +852,7 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
     gemm_big_bf16<EPI, BG_DK, BG_NSTG><<<dim3(p.ntn, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e);
   } else {
-    gemm_tiled_bf16<EPI><<<dim3(p.ntn, p.ntm, p.splits), 256, 0, st>>>(
+    gemm_tiled_bf16<EPI><<<dim3(p.ntm, p.ntn, p.splits), 256, 0, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, counters,
         e);
   }
