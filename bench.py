@@ -193,19 +193,10 @@ def _graph_time(torch, launch_all, n_launch: int, rounds: int) -> float:
     return e0.elapsed_time(e1) * 1e3 / (rounds * n_launch)
 
 
-def kernel_only(lib, torch, bd, rounds: int = 10):
-    """Kernel-only workload at the 8B step shape: block attention of 32 query rows per
-    head (32 heads x 128) against 1024 cached keys, and the confidence/unmask pass over
-    [32, 126464] bf16 logits (N(0,1) plus a U(0,12) boost at one id per row, tau 0.9,
-    all 32 positions masked).  Launches rotate through buffer sets totalling more than
-    the 256 MB Infinity Cache and are replayed from a HIP graph; the time per launch is
-    HIP events around the replays divided by the launches (so it includes the short gaps
-    between kernels, and for the confidence entry its counter-reset kernel)."""
-    out = {}
-    # ---- attention
-    B, Hq, Hkv, R, S, D = 1, 32, 32, 32, 1024, 128
+def _attn_rate(lib, torch, bd, S: int, nset: int, rounds: int, B=1, Hq=32, Hkv=32, R=32, D=128):
+    """Block attention of R query rows per head against S cached keys, bf16, q/k/v
+    N(0, 1) from the seeded device generator; nset buffer sets rotated per replay."""
     Sp = (S + 63) // 64 * 64
-    nset = 20
     sets = []
     st0 = bd.stream_handle()
     for i in range(nset):
@@ -227,37 +218,71 @@ def kernel_only(lib, torch, bd, rounds: int = 10):
                      wsb, st)
     us = _graph_time(torch, attn_all, nset, rounds)
     nbytes = (B * Hq * R * D * 2) * 2 + B * Hkv * S * D * 2 * 2
-    out["attention"] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
-                        "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "sets": nset,
-                        "shape": "B1 H32x128 q32 kv1024 bf16"}
-    del sets
-    # ---- confidence / unmask
-    K, V, mask_id, tau = 32, 126464, 126463, 0.9
-    host = synth.boosted_logits(43, K, V, 12.0, "bf16")
-    one = torch.from_numpy(host.view(np.int16)).to("cuda")
-    nset = 40
-    logits = [one.clone() for _ in range(nset)]
-    toks = torch.full((nset, K), mask_id, dtype=torch.int32, device="cuda")
-    conf = torch.empty(K, dtype=torch.float32, device="cuda")
-    arg = torch.empty(K, dtype=torch.int32, device="cuda")
-    nun = torch.empty(1, dtype=torch.int32, device="cuda")
-    rem = torch.empty(1, dtype=torch.int32, device="cuda")
-    uidx = torch.empty(K, dtype=torch.int32, device="cuda")
-    wsb = lib.raw("dllm_kernel_workspace_bytes")(1, 0, 0, 0, 0, K, V)
+    return {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+            "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "sets": nset,
+            "shape": f"B{B} H{Hq}x{D} q{R} kv{S} bf16"}
+
+
+def _conf_rate(lib, torch, bd, B: int, K: int, V: int, ldtype: str, nset: int, rounds: int,
+               logits_of=None):
+    """Confidence/unmask over B sequences of K block rows (all masked, tau 0.9); logits
+    from logits_of(i) or N(0, 1) from the seeded device generator."""
+    mask_id, tau = V - 1, 0.9
+    dt = 1 if ldtype == "bf16" else 0
+    tdt = torch.int16 if ldtype == "bf16" else torch.float32
+    logits = []
+    for i in range(nset):
+        if logits_of is not None:
+            logits.append(logits_of(i))
+        else:
+            z = torch.empty(B * K * V, dtype=tdt, device="cuda")
+            lib.call("dllm_synth_fill", bd.ptr(z), z.numel(), dt, 43 + i, 0xB010, 1.0, 0,
+                     bd.stream_handle())
+            logits.append(z)
+    toks = torch.full((nset, B * K), mask_id, dtype=torch.int32, device="cuda")
+    conf = torch.empty(B * K, dtype=torch.float32, device="cuda")
+    arg = torch.empty(B * K, dtype=torch.int32, device="cuda")
+    nun = torch.empty(B, dtype=torch.int32, device="cuda")
+    rem = torch.empty(B, dtype=torch.int32, device="cuda")
+    uidx = torch.empty(B * K, dtype=torch.int32, device="cuda")
+    wsb = lib.raw("dllm_kernel_workspace_bytes")(B, 0, 0, 0, 0, K, V)
     ws = torch.zeros(max(wsb, 1), dtype=torch.uint8, device="cuda")
 
     def conf_all():
         st = bd.stream_handle()
-        toks.fill_(mask_id)             # every launch sees a fully masked block
+        toks.fill_(mask_id)             # every launch sees fully masked blocks
         for i in range(nset):
-            lib.call("dllm_kernel_confidence_unmask", bd.ptr(logits[i]), 1, 1, K, V, mask_id,
+            lib.call("dllm_kernel_confidence_unmask", bd.ptr(logits[i]), dt, B, K, V, mask_id,
                      tau, bd.ptr(toks[i]), K, bd.ptr(conf), bd.ptr(arg), bd.ptr(nun),
                      bd.ptr(rem), bd.ptr(uidx), bd.ptr(ws), wsb, st)
     us = _graph_time(torch, conf_all, nset, rounds)
-    nbytes = K * V * 2
-    out["confidence"] = {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
-                         "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "sets": nset,
-                         "shape": "[32, 126464] bf16 logits, tau 0.9"}
+    nbytes = B * K * V * (2 if ldtype == "bf16" else 4)
+    return {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 1),
+            "frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "sets": nset,
+            "shape": f"[{B * K}, {V}] {ldtype} logits, tau 0.9"}
+
+
+def kernel_only(lib, torch, bd, rounds: int = 10):
+    """Kernel-only rates.  The 8B step shape: block attention of 32 query rows per head
+    (32 heads x 128) against 1024 cached keys, and the confidence/unmask pass over
+    [32, 126464] bf16 logits (N(0,1) plus a U(0,12) boost at one id per row, tau 0.9, all
+    32 positions masked).  Both are small enough to be bound by launch and DRAM latency,
+    so the same kernels are also timed where bandwidth binds: attention against 16384
+    cached keys (268 MB of K/V), and the confidence pass over the 7B shape's batch of 8
+    blocks, [256, 152064] fp32 logits (156 MB).  Launches rotate through buffer sets
+    totalling more than the 256 MB Infinity Cache and are replayed from a HIP graph; the
+    time per launch is HIP events around the replays divided by the launches (so it
+    includes the short gaps between kernels)."""
+    out = {"attention": _attn_rate(lib, torch, bd, 1024, 20, rounds)}
+    torch.cuda.empty_cache()
+    out["attention_16k_keys"] = _attn_rate(lib, torch, bd, 16384, 3, rounds)
+    torch.cuda.empty_cache()
+    host = synth.boosted_logits(43, 32, 126464, 12.0, "bf16")
+    one = torch.from_numpy(host.view(np.int16)).to("cuda")
+    out["confidence"] = _conf_rate(lib, torch, bd, 1, 32, 126464, "bf16", 40, rounds,
+                                   logits_of=lambda i: one.clone())
+    torch.cuda.empty_cache()
+    out["confidence_7b_batch8"] = _conf_rate(lib, torch, bd, 8, 32, 152064, "f32", 3, rounds)
     return out
 
 
