@@ -489,6 +489,20 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
         for (int j = 0; j < 2; ++j)
           acc[i][j] = mfma32(as_bf16x8(a[kk & 1][i]), as_bf16x8(b[kk & 1][j]), acc[i][j]);
     }
+    // Pin the issue order: the six operand reads of step 0, then for each step the next
+    // step's reads alternating with this step's MFMAs.  Left alone, the scheduler reuses
+    // one operand register set and waits for every read before each MFMA group.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // 0x100: LDS reads
+#pragma unroll
+    for (int kk = 0; kk < DK / 16 - 1; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
   // s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left at their maximum)
 #define DLLM_VMWAIT(n) \
