@@ -21,6 +21,8 @@
 //     LDS with register prefetch, 4 waves each computing 64x64 with 32x32x16 MFMAs; the
 //     same split-K schemes for shapes with too few tiles.
 //   gemm_f32: SIMT fp32 kernel for fp32 models (32x128 tiles).
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,6 +39,8 @@ __device__ __forceinline__ int wrow_of(int vc, int F) {
 }
 
 __device__ __forceinline__ float silu(float x) { return x / (1.f + expf(-x)); }
+// SwiGLU output value of one row and column from its gate and up sums.
+__device__ __forceinline__ uint16_t swiglu_bf16(float gt, float up) { return f2bf(silu(gt) * up); }
 
 __device__ __forceinline__ int acc_row(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
 
@@ -554,6 +558,199 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
 }
 
 // ============================================================================
+// mid-size bf16 GEMM (kSkinnyRows < M <= 256: a batch of block steps, or the block and
+// suffix rows of a prefix-mode step)
+// ============================================================================
+// One 256-row tile covers every row, so each weight tile is read once.  Output tiles are
+// 128 virtual columns wide (the 64-column virtual order of wrow_s2, so split partials
+// go through reduce_epilogue unchanged).  8 waves, 4 (rows) x 2 (columns), each 64 x 64
+// with 2 x 2 32x32x16 MFMAs; K stages of 64 in a ring of three LDS slots filled by direct
+// global->LDS loads two stages ahead; one barrier per stage.
+// Work units, walked persistently by at most one workgroup per CU:
+//   * units [0, ndp): whole tiles 0 .. ndp-1, full K, epilogue from an LDS tile;
+//   * then every tile t >= ndp in `splits` K pieces of kst stages: fp32 partials
+//     [split][M][Nv - 128 ndp], summed in split order by reduce_epilogue (or, residual
+//     GEMMs, by the next RMSNorm).
+// The plan splits everything for the residual and QKV GEMMs and, for the others, only the
+// ragged last round of tiles, so the chip stays busy without a partial round trip for
+// the bulk of the work.
+constexpr int MD_BN = 128, MD_DK = 64, MD_NSTG = 3, MD_THREADS = 512;
+constexpr int MD_A = kMidRows * MD_DK * 2;  // A (activation) bytes per stage
+constexpr int MD_STG = MD_A + MD_BN * MD_DK * 2;
+constexpr int MD_SMEM = MD_NSTG * MD_STG;   // 144 KB
+constexpr int MD_TL = 132;                  // row stride (floats) of the epilogue tile
+static_assert(kMidRows * MD_TL * 4 <= MD_SMEM, "epilogue tile fits in the operand ring");
+
+// Epilogue of a whole tile in LDS (rows 0..255, tile-local virtual columns 0..127 at
+// vc0) in wrow_s2's virtual order.  Only STORE, F32 and SWIGLU tiles are whole.
+template <int EPI>
+__device__ void mid_epilogue(const float* tile, int M, int vc0, int Nv, const EpiArgs& e) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // 64 outputs per row: column c of the tile's span takes gate 64(c/32) + c%32, up +32
+    for (int i = threadIdx.x; i < kMidRows * 64; i += blockDim.x) {
+      const int m = i >> 6, c = i & 63;
+      const int vg = 64 * (c >> 5) + (c & 31);
+      if (m >= M || vc0 + vg >= Nv) continue;
+      ((uint16_t*)e.y)[(int64_t)m * e.F + vc0 / 2 + c] =
+          swiglu_bf16(tile[m * MD_TL + vg], tile[m * MD_TL + vg + 32]);
+    }
+  } else if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
+    epilogue<uint16_t, EPI>(tile, MD_TL, kMidRows, 0, vc0, M, Nv, e);
+  }
+  // residual and QKV GEMMs are always split (the plan gives them no whole tiles)
+}
+
+template <int MAP, int EPI>
+__global__ __launch_bounds__(MD_THREADS, 1) void gemm_mid_bf16(
+    const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv, int K,
+    int ndp, int splits, int kst, int nunits, float* __restrict__ part, EpiArgs e) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char md_smem[];
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, wm = w & 3, wn = w >> 2, l = tid & 63, lr = l & 31, g = l >> 5;
+  const int Nt = Nv - ndp * MD_BN;  // row stride of the partials
+  // 16-byte chunk c of tile row r sits in slot c ^ (r & 7) of the row's 128 bytes, so
+  // the operand reads (32 rows at one k offset) spread over all banks
+  auto swz = [](int r) { return r & 7; };
+
+  for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
+    const bool whole = u < ndp;
+    int tile = u, split = 0, kb = 0, ke = K;
+    if (!whole) {
+      const int v = u - ndp;
+      tile = ndp + v / splits;
+      split = v % splits;
+      kb = split * kst * MD_DK;
+      ke = min(K, kb + kst * MD_DK);
+    }
+    const int vc0 = tile * MD_BN;
+    const int nst = (ke - kb) / MD_DK;
+
+    // wave w fills A rows 32w .. +32 and B rows 16w .. +16, 8 rows per load instruction
+    // (lane l: row + l/8, chunk slot l%8); rows past M / columns past Nv read a clamped
+    // valid row whose results are never stored
+    const uint16_t* asrc[4];
+    const uint16_t* bsrc[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 32 * w + 8 * i + (l >> 3);
+      asrc[i] = X + (int64_t)min(row, M - 1) * ldx + kb + ((l & 7) ^ swz(row)) * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = 16 * w + 8 * i + (l >> 3);
+      bsrc[i] = W + (int64_t)wrow_s2<MAP>(min(vc0 + row, Nv - 1), e.F) * K + kb +
+                ((l & 7) ^ swz(row)) * 8;
+    }
+    auto issue = [&](int st) {
+      unsigned char* base = md_smem + (st % MD_NSTG) * MD_STG;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(asrc[i] + st * MD_DK),
+            (__attribute__((address_space(3))) void*)(base + (32 * w + 8 * i) * (MD_DK * 2)), 16,
+            0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(bsrc[i] + st * MD_DK),
+            (__attribute__((address_space(3))) void*)(base + MD_A + (16 * w + 8 * i) * (MD_DK * 2)),
+            16, 0, 0);
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto frag = [&](int slot, int kk, u32x4* a, u32x4* b) {
+      const unsigned char* base = md_smem + slot * MD_STG;
+      const int c = 2 * kk + g;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 64 * wm + 32 * i + lr;
+        a[i] = *reinterpret_cast<const u32x4*>(base + r * (MD_DK * 2) + ((c ^ swz(r)) * 16));
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = 64 * wn + 32 * j + lr;
+        b[j] = *reinterpret_cast<const u32x4*>(base + MD_A + r * (MD_DK * 2) + ((c ^ swz(r)) * 16));
+      }
+    };
+    auto compute = [&](int slot) {
+      u32x4 a[2][2], b[2][2];
+      frag(slot, 0, a[0], b[0]);
+#pragma unroll
+      for (int kk = 0; kk < MD_DK / 16; ++kk) {
+        if (kk + 1 < MD_DK / 16) frag(slot, kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = mfma32(as_bf16x8(a[kk & 1][i]), as_bf16x8(b[kk & 1][j]), acc[i][j]);
+      }
+      // issue order: the four operand reads of step 0, then the next step's reads
+      // alternating with this step's MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 0x100: LDS reads
+#pragma unroll
+      for (int kk = 0; kk < MD_DK / 16 - 1; ++kk) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 0x008: MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    // s_waitcnt with only vmcnt = n (expcnt and lgkmcnt left at their maximum)
+#define DLLM_VMWAIT(n) \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+    for (int st = 0; st < MD_NSTG - 1 && st < nst; ++st) issue(st);
+    for (int st = 0; st < nst; ++st) {
+      // this wave's loads of stage st have landed once at most the 6 loads of stage
+      // st + 1 are still in flight; the barrier then covers every wave's, and every wave
+      // is done with the slot that stage st + 2 refills
+      if (st + 1 < nst) DLLM_VMWAIT(6);
+      else DLLM_VMWAIT(0);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (st + MD_NSTG - 1 < nst) issue(st + MD_NSTG - 1);
+      compute(st % MD_NSTG);
+    }
+#undef DLLM_VMWAIT
+    __syncthreads();  // the operand ring is free: the epilogue tile and the next unit reuse it
+
+    // accumulator (i, j, v): tile row 64 wm + 32 i + acc_row(v, g), column 64 wn + 32 j + lr
+    if (whole) {
+      float* t = reinterpret_cast<float*>(md_smem);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            t[(64 * wm + 32 * i + acc_row(v, g)) * MD_TL + 64 * wn + 32 * j + lr] = acc[i][j][v];
+      __syncthreads();
+      mid_epilogue<EPI>(t, M, vc0, Nv, e);
+      __syncthreads();
+    } else {
+      float* pp = part + (int64_t)split * M * Nt;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int vc = vc0 + 64 * wn + 32 * j + lr;
+        if (vc >= Nv) continue;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = 64 * wm + 32 * i + acc_row(v, g);
+            if (r < M) pp[(int64_t)r * Nt + (vc - ndp * MD_BN)] = acc[i][j][v];
+          }
+      }
+    }
+  }
+}
+
+// ============================================================================
 // fp32 SIMT GEMM (fp32 models): 32x128 tiles, K % 16 == 0
 // ============================================================================
 template <int EPI>
@@ -637,15 +834,39 @@ __device__ __forceinline__ float4 scale4(float4 v, float r) {
   return make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
 }
 
+// One RoPE pair of the QKV epilogue (head_dim 128): head slot hs (q heads, then k, then
+// v), dims d and d + 64 of row m, with the sums x1 and x2.  q and k are rotated at the
+// row's position; v is written to the transposed cache.
+__device__ __forceinline__ void qkv_pair(const EpiArgs& e, int m, int hs, int d, float x1,
+                                         float x2) {
+  const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
+  if (hs < e.Hq + e.Hkv) {
+    uint16_t* dst = (hs < e.Hq)
+        ? (uint16_t*)e.qo + (((int64_t)bs * e.Hq + hs) * e.R + ri) * 128
+        : (uint16_t*)e.kc + (((int64_t)bs * e.Hkv + (hs - e.Hq)) * e.Sp + pos) * 128;
+    const float cs = e.rcos[(int64_t)pos * 64 + d], sn = e.rsin[(int64_t)pos * 64 + d];
+    dst[d] = f2bf(x1 * cs - x2 * sn);
+    dst[d + 64] = f2bf(x2 * cs + x1 * sn);
+  } else {
+    uint16_t* dst = (uint16_t*)e.vtc + ((int64_t)bs * e.Hkv + (hs - e.Hq - e.Hkv)) * 128 * (int64_t)e.Sp;
+    dst[(int64_t)d * e.Sp + pos] = f2bf(x1);
+    dst[(int64_t)(d + 64) * e.Sp + pos] = f2bf(x2);
+  }
+}
+
+// Split-K reduction + epilogue over the partial columns [0, pv.N), i.e. the virtual
+// output columns [pv.vbase, pv.vbase + pv.N), in the 64-column virtual order of
+// wrow_s2 (SwiGLU: 32 gate columns then the matching 32 up columns; QKV: one head slot
+// per 128 columns, dims 0..31, 64..95, 32..63, 96..127).
 template <int EPI>
 __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
-  const int M = pv.M, Nv = pv.N;
+  const int M = pv.M, Nt = pv.N;
   const int64_t i4 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
   if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
-    // Nv % 4 == 0: 4 outputs of one row
-    if (i4 >= (int64_t)M * Nv) return;
-    const int m = (int)(i4 / Nv), vc = (int)(i4 % Nv);
-    const float4 v = scale4(sum_split4(pv, m, vc), row_rms_factor(e, m));
+    // Nt % 4 == 0: 4 outputs of one row
+    if (i4 >= (int64_t)M * Nt) return;
+    const int m = (int)(i4 / Nt), c = (int)(i4 % Nt), vc = pv.vbase + c;
+    const float4 v = scale4(sum_split4(pv, m, c), row_rms_factor(e, m));
     if constexpr (EPI == EPI_F32) {
       float4 o = make_float4(v.x * e.scale, v.y * e.scale, v.z * e.scale, v.w * e.scale);
       *reinterpret_cast<float4*>((float*)e.y + (int64_t)m * e.ldy + vc) = o;
@@ -654,54 +875,40 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
       y[0] = f2bf(v.x); y[1] = f2bf(v.y); y[2] = f2bf(v.z); y[3] = f2bf(v.w);
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
-    // output column c of row m: gate at virtual column 64(c/32) + c%32, up 32 further
-    if (i4 >= (int64_t)M * e.F) return;
-    const int m = (int)(i4 / e.F), c = (int)(i4 % e.F);
+    // output column c of the span: gate at partial column 64(c/32) + c%32, up 32 further
+    const int nout = Nt / 2;
+    if (i4 >= (int64_t)M * nout) return;
+    const int m = (int)(i4 / nout), c = (int)(i4 % nout);
     const int vg = 64 * (c >> 5) + (c & 31);
     const float r = row_rms_factor(e, m);
     const float4 gt = scale4(sum_split4(pv, m, vg), r);
     const float4 up = scale4(sum_split4(pv, m, vg + 32), r);
-    uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.F + c;
-    y[0] = f2bf(silu(gt.x) * up.x); y[1] = f2bf(silu(gt.y) * up.y);
-    y[2] = f2bf(silu(gt.z) * up.z); y[3] = f2bf(silu(gt.w) * up.w);
+    uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.F + pv.vbase / 2 + c;
+    y[0] = swiglu_bf16(gt.x, up.x); y[1] = swiglu_bf16(gt.y, up.y);
+    y[2] = swiglu_bf16(gt.z, up.z); y[3] = swiglu_bf16(gt.w, up.w);
   } else if constexpr (EPI == EPI_QKV) {
     // (row m, head slot hs, dims d..d+3 < 64) -> pairs (d, d+64); head_dim 128
-    const int nslot = Nv / 128;
+    const int nslot = Nt / 128;
     if (i4 >= (int64_t)M * nslot * 64) return;
     const int m = (int)(i4 / (nslot * 64));
     const int rem = (int)(i4 % (nslot * 64));
-    const int hs = rem / 64, d = rem % 64;
-    const int vc = 64 * (2 * hs + (d >> 5)) + (d & 31);
+    const int hl = rem / 64, d = rem % 64;
+    const int c = 64 * (2 * hl + (d >> 5)) + (d & 31);
     const float r = row_rms_factor(e, m);
-    const float4 a = scale4(sum_split4(pv, m, vc), r);
-    const float4 b = scale4(sum_split4(pv, m, vc + 32), r);
-    const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
-    float x1[4] = {a.x, a.y, a.z, a.w}, x2[4] = {b.x, b.y, b.z, b.w};
-    if (hs < e.Hq + e.Hkv) {
-      uint16_t* dst = (hs < e.Hq)
-          ? (uint16_t*)e.qo + (((int64_t)bs * e.Hq + hs) * e.R + ri) * 128
-          : (uint16_t*)e.kc + (((int64_t)bs * e.Hkv + (hs - e.Hq)) * e.Sp + pos) * 128;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float cs = e.rcos[(int64_t)pos * 64 + d + u], sn = e.rsin[(int64_t)pos * 64 + d + u];
-        dst[d + u] = f2bf(x1[u] * cs - x2[u] * sn);
-        dst[d + u + 64] = f2bf(x2[u] * cs + x1[u] * sn);
-      }
-    } else {
-      uint16_t* dst = (uint16_t*)e.vtc + ((int64_t)bs * e.Hkv + (hs - e.Hq - e.Hkv)) * 128 * (int64_t)e.Sp;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        dst[(int64_t)(d + u) * e.Sp + pos] = f2bf(x1[u]);
-        dst[(int64_t)(d + u + 64) * e.Sp + pos] = f2bf(x2[u]);
-      }
-    }
+    const float4 a = scale4(sum_split4(pv, m, c), r);
+    const float4 b = scale4(sum_split4(pv, m, c + 32), r);
+    const int hs = pv.vbase / 128 + hl;
+    qkv_pair(e, m, hs, d + 0, a.x, b.x);
+    qkv_pair(e, m, hs, d + 1, a.y, b.y);
+    qkv_pair(e, m, hs, d + 2, a.z, b.z);
+    qkv_pair(e, m, hs, d + 3, a.w, b.w);
   }
 }
 
 hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e, hipStream_t st) {
   int64_t n4 = 0;
   if (epi == EPI_STORE || epi == EPI_F32) n4 = (int64_t)pv.M * pv.N / 4;
-  else if (epi == EPI_SWIGLU) n4 = (int64_t)pv.M * e.F / 4;
+  else if (epi == EPI_SWIGLU) n4 = (int64_t)pv.M * (pv.N / 2) / 4;
   else if (epi == EPI_QKV) n4 = (int64_t)pv.M * (pv.N / 128) * 16;
   else return hipErrorInvalidValue;
   if (n4 <= 0) return hipSuccess;
@@ -718,6 +925,21 @@ hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e,
 // ============================================================================
 // planning and dispatch
 // ============================================================================
+// compute units of the current device (256 on MI355X; 256 when no device is visible)
+static int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      n = cus;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   GemmPlan p;
   if (dtype == F32) {
@@ -742,6 +964,39 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     p.splits = K / p.kchunk;
     p.part_floats = (size_t)p.splits * ((Nv + 15) / 16) * (p.mt * 16 * 16);  // blocked layout
     p.deferred = true;  // partials reduced by the next RMSNorm or by reduce_epilogue
+    p.reduce = (epi != EPI_RESID);
+    return p;
+  }
+  if (M <= kMidRows && K % MD_DK == 0) {
+    // one 256-row tile: residual and QKV GEMMs split every tile over K into about one
+    // unit per CU; the others run whole tiles and split only a ragged last round
+    p.kind = GEMM_MID;
+    const int P = num_cus();
+    const int tiles = (Nv + MD_BN - 1) / MD_BN;
+    const int ns = K / MD_DK;
+    int S = 1, ndp = 0;
+    if (epi == EPI_RESID || epi == EPI_QKV) {
+      S = P / tiles;
+    } else {
+      const int tail = tiles % P;
+      // the reduction of a split tail reads float4 columns
+      S = (tail > 0 && Nv % 4 == 0) ? P / tail : 1;
+      ndp = (S <= 1) ? tiles : tiles - tail;
+    }
+    S = std::max(1, std::min(S, ns));
+    const int kst = (ns + S - 1) / S;  // stages per split; no split is empty
+    S = (ns + kst - 1) / kst;
+    p.ntn = tiles;
+    p.ntm = 1;
+    p.splits = S;
+    p.kchunk = kst * MD_DK;
+    p.ndp = ndp;
+    p.units = ndp + (tiles - ndp) * S;
+    if (ndp < tiles) {
+      p.part_floats = (size_t)S * M * (Nv - ndp * MD_BN);
+      p.deferred = true;
+      p.reduce = (epi != EPI_RESID);
+    }
     return p;
   }
   // large GEMMs: 256x256 tiles unless their count fills the chip much worse than the
@@ -804,20 +1059,6 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   return p;
 }
 
-static int num_cus() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0)
-      n = cus;
-    else
-      n = 256;
-  }
-  return n;
-}
-
 template <int EPI>
 static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ldx, const void* W,
                              int M, int Nv, int K, const EpiArgs& e, float* part, int* counters,
@@ -854,6 +1095,19 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
       else DLLM_SKINNY(4, 32);
     }
 #undef DLLM_SKINNY
+  } else if (p.kind == GEMM_MID) {
+    constexpr int MAP = (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? EPI : EPI_STORE;
+    static bool mid_attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
+    if (!mid_attr_set) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mid_bf16<MAP, EPI>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, MD_SMEM);
+      if (err != hipSuccess) return err;
+      mid_attr_set = true;
+    }
+    const int grid = std::min(p.units, num_cus());
+    gemm_mid_bf16<MAP, EPI><<<grid, MD_THREADS, MD_SMEM, st>>>(
+        (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.ndp, p.splits,
+        p.kchunk / MD_DK, p.units, part, e);
   } else if (p.kind == GEMM_BIG) {
     static bool attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
     if (!attr_set) {
@@ -879,8 +1133,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int
   if (M <= 0 || Nv <= 0) return hipSuccess;
   hipError_t err = launch_gemm_only(dtype, epi, p, X, ldx, W, M, Nv, K, e, part, counters, st);
   if (err != hipSuccess) return err;
-  if (p.kind == GEMM_SKINNY && epi != EPI_RESID)
-    return launch_reduce_epilogue(epi, p.view(part, M, Nv), e, st);
+  if (p.reduce) return launch_reduce_epilogue(epi, p.view(part, M, Nv), e, st);
   return hipSuccess;
 }
 

@@ -39,20 +39,23 @@ struct EpiArgs {
   float reps = 0.f;
 };
 
-enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3 };
+enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3, GEMM_MID = 4 };
 constexpr int kSkinnyRows = 64;  // bf16 GEMMs with at most this many rows stream weights
+constexpr int kMidRows = 256;    // above kSkinnyRows and up to this many: one 256-row tile
 
 // Where split-K partial sums live.  Plain: [split][M][N].  Blocked (skinny GEMM): per split,
 // per 16-column group, one block of mrows x 16 floats in which row m, column c sits at
 // ((mt*4 + r)*4 + g)*16 + c with m = 16 mt + 4 g + r, so that every store instruction of
 // the producing wave writes 256 contiguous bytes.  Four consecutive columns starting at a
-// multiple of 4 are contiguous in both layouts.
+// multiple of 4 are contiguous in both layouts.  Partial column c is the GEMM's virtual
+// output column vbase + c (vbase > 0 when only the trailing tiles were split).
 struct PartView {
   const float* p = nullptr;
   int splits = 0;
   int blocked = 0;
   int mrows = 0;        // blocked: rows per block (16, 32 or 64)
   int M = 0, N = 0;     // plain: row stride is N
+  int vbase = 0;        // a multiple of 128
   __host__ __device__ int64_t split_stride() const {
     return blocked ? (int64_t)((N + 15) / 16) * mrows * 16 : (int64_t)M * N;
   }
@@ -71,17 +74,22 @@ struct GemmPlan {
   size_t part_floats = 0;  // split-K partial buffer
   int counters = 0;        // split-K arrival counters
   bool deferred = false;   // residual partials left for the next RMSNorm to add
+  bool reduce = false;     // a reduce_epilogue launch finishes the split columns
+  int ndp = 0;             // mid: leading tiles computed whole (direct epilogue)
+  int units = 0;           // mid: work units (whole tiles, then tile x K-split pieces)
   PartView view(const float* part, int M, int N) const {
     PartView v;
-    v.p = part; v.splits = splits; v.M = M; v.N = N;
+    v.p = part; v.splits = splits; v.M = M;
     v.blocked = (kind == GEMM_SKINNY);
     v.mrows = mt * 16;
+    v.vbase = (kind == GEMM_MID) ? ndp * 128 : 0;
+    v.N = N - v.vbase;
     return v;
   }
 };
 
 GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi);
-// launch_gemm = launch_gemm_only + (skinny, non-residual) launch_reduce_epilogue
+// launch_gemm = launch_gemm_only + launch_reduce_epilogue when the plan asks for it
 hipError_t launch_gemm(int dtype, int epi, const GemmPlan& p, const void* X, int ldx,
                        const void* W, int M, int Nv, int K, const EpiArgs& e, float* part,
                        int* counters, hipStream_t st);

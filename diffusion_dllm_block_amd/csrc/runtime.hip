@@ -284,7 +284,7 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
     HIP_TRY(launch_gemm_only(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, er, c.at<float>(c.w.gpart),
                              c.at<int>(c.w.gcnt), c.st));
   }
-  if (p.kind == GEMM_SKINNY && epi != EPI_RESID) {
+  if (p.reduce) {
     ProfScope ps(DLLM_K_SPLIT_REDUCE, c.st);
     HIP_TRY(launch_reduce_epilogue(epi, p.view(c.at<float>(c.w.gpart), M, Nv), er, c.st));
   }

@@ -224,13 +224,19 @@ def run_linear(lib, x, w, M, N, K, dtype, mode, scale=1.0, y0=None):
 
 
 GEMM_CASES = [
-    # name, M, N, K, dtype   (skinny: M <= 64; tiled: 64 < M < 512; big: M >= 512)
+    # name, M, N, K, dtype   (skinny: M <= 64; mid: 64 < M <= 256; tiled: 256 < M < 512;
+    # big: M >= 512)
     ("skinny_m32_o_proj", 32, 4096, 4096, "bf16"),
     ("skinny_m7_ragged_n", 7, 1000, 512, "bf16"),
     ("skinny_m50_two_tiles", 50, 384, 1024, "bf16"),
     ("skinny_m32_down_k12288", 32, 512, 12288, "bf16"),
     ("tiled_m300_ragged", 300, 384, 512, "bf16"),
-    ("tiled_m256_splitk", 256, 256, 3584, "bf16"),
+    # mid (64 < M <= 256): every tile split over K / whole tiles plus a split ragged
+    # last round (2 rounds of 256 whole tiles, 9 tail tiles in 4 K pieces) / ragged N
+    ("mid_m256_deep_splitk", 256, 256, 3584, "bf16"),
+    ("mid_m96_ragged_n", 96, 1000, 512, "bf16"),
+    ("mid_m200_whole_and_tail", 200, 33000, 256, "bf16"),
+    ("mid_m130_rounds_and_tail", 130, 66624, 256, "bf16"),
     ("big_m600_ragged_splitk", 600, 640, 512, "bf16"),
     ("big_m1064_two_row_tiles", 1064, 768, 1024, "bf16"),
     ("f32_small", 20, 200, 64, "f32"),
