@@ -37,17 +37,21 @@ __device__ __forceinline__ bf16x8 pack_p(const float* p, int u) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// 8 bf16 at keys k..k+7 (k % 8 == 0) of a Vt row, one 16-byte load; keys >= S read as
-// zero (clamped address, masked value).
-__device__ __forceinline__ bf16x8 load8_masked(const uint16_t* row, int k, int S, int Sp) {
-  const u32x4 v = *reinterpret_cast<const u32x4*>(row + min(k, Sp - 8));
-  const int n = S - k;
+// 8 bf16 at keys k..k+7 (k % 8 == 0) of a Vt row: one 16-byte load from a clamped
+// address (Sp % 8 == 0, so every key below S is read from its own place) ...
+__device__ __forceinline__ u32x4 load8_raw(const uint16_t* row, int k, int Sp) {
+  return *reinterpret_cast<const u32x4*>(row + min(k, Sp - 8));
+}
+// ... and, where the 8 keys may reach S, the keys >= S zeroed (n = S - k).  The mask is
+// applied where the value is used, not right after the load: masking at the load would
+// make the wave wait for a prefetch it does not need yet.
+__device__ __forceinline__ u32x4 mask8(const u32x4& v, int n) {
   auto keep = [](int c) {  // c elements of 4 kept
     return c >= 4 ? ~0ull : (c <= 0 ? 0ull : (1ull << (16 * c)) - 1ull);
   };
   const uint64_t lo = (((uint64_t)v[1] << 32) | v[0]) & keep(n);
   const uint64_t hi = (((uint64_t)v[3] << 32) | v[2]) & keep(n - 4);
-  return as_bf16x8(u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)});
+  return u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
 }
 
 // ============================================================================
@@ -74,7 +78,7 @@ constexpr int QS_LD = HD + 8;   // LDS row stride (elements) of the staged Q til
 
 struct KVTile16 {
   u32x4 k[2][4];  // [tau][k-step]: K row of key 8(i/4) + 4 tau + i%4, dims 32 s + 8j
-  u32x4 v[8];     // [d-tile]: Vt row 16 dt + l%16, keys 8j .. 8j+7
+  u32x4 v[8];     // [d-tile]: Vt row 16 dt + l%16, keys 8j .. 8j+7 (unmasked)
 };
 
 __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
@@ -89,10 +93,7 @@ __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
     for (int st = 0; st < 4; ++st) t.k[tau][st] = *reinterpret_cast<const u32x4*>(kp + 32 * st);
   }
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
-    const bf16x8 v = load8_masked(vbase + (int64_t)(16 * dt + li) * Sp, key0 + 8 * j, S, Sp);
-    t.v[dt] = __builtin_bit_cast(u32x4, v);
-  }
+  for (int dt = 0; dt < 8; ++dt) t.v[dt] = load8_raw(vbase + (int64_t)(16 * dt + li) * Sp, key0 + 8 * j, Sp);
 }
 
 // ONE: every wave has a single 32-key sub-tile (nsub == 1): one operand tile in
@@ -189,10 +190,14 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
 #pragma unroll
       for (int e = 0; e < 8; ++e) pb[e] = f2bf(p[e]);
       const bf16x8 pop = __builtin_bit_cast(bf16x8, pb);
+      // keys >= S: their P is 0, and their Vt values (read from clamped or padding
+      // positions) are zeroed so that no stale NaN/Inf reaches the product
+      const bool tail = key0 + 32 > S;  // uniform over the wave
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         oacc[qq][dt] *= alpha;
-        oacc[qq][dt] = mfma16(as_bf16x8(t.v[dt]), pop, oacc[qq][dt]);
+        const u32x4 vv = tail ? mask8(t.v[dt], S - (key0 + 8 * j)) : t.v[dt];
+        oacc[qq][dt] = mfma16(as_bf16x8(vv), pop, oacc[qq][dt]);
       }
     }
   };
@@ -200,13 +205,15 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
   if constexpr (ONE) {
     consume(ta, wkey0);
   } else {
+    // The next sub-tile is always requested, past the end too (clamped addresses, never
+    // consumed): with no load under a branch, the wait before each consume counts only
+    // the sub-tile it needs, and the following one stays in flight.
     KVTile16 tb;
     for (int n = 0; n < nsub; n += 2) {
-      if (n + 1 < nsub) load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
+      load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
       consume(ta, wkey0 + 32 * n);
-      if (n + 1 >= nsub) break;
-      if (n + 2 < nsub) load_kv16(ta, kbase, vbase, wkey0 + 32 * (n + 2), li, j, S, Sp);
-      consume(tb, wkey0 + 32 * (n + 1));
+      load_kv16(ta, kbase, vbase, wkey0 + 32 * (n + 2), li, j, S, Sp);
+      if (n + 1 < nsub) consume(tb, wkey0 + 32 * (n + 1));
     }
   }
 
@@ -373,21 +380,26 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
     for (int i = 0; i < 4; ++i) {
       const int e = threadIdx.x + 256 * i;
       const int r = e >> 3, c8 = e & 7;   // Vt: 128 rows x 8 chunks of 8 keys
-      vreg[i] = __builtin_bit_cast(u32x4, load8_masked(vb + (int64_t)r * Sp, kbase + 8 * c8, S, Sp));
+      vreg[i] = load8_raw(vb + (int64_t)r * Sp, kbase + 8 * c8, Sp);
     }
   };
   load_tile(0);
   for (int kt = 0; kt < ntile; ++kt) {
     const int kbase = kt * FK;
     __syncthreads();  // every wave is done with the previous tile
+    const bool tail = kbase + FK > S;  // uniform: the Vt keys >= S are zeroed
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = threadIdx.x + 256 * i;
       *reinterpret_cast<u32x4*>(&Ks[(e >> 4) * KS_LD + 8 * (e & 15)]) = kreg[i];
-      *reinterpret_cast<u32x4*>(&Vs[(e >> 3) * VS_LD + 8 * (e & 7)]) = vreg[i];
+      *reinterpret_cast<u32x4*>(&Vs[(e >> 3) * VS_LD + 8 * (e & 7)]) =
+          tail ? mask8(vreg[i], S - (kbase + 8 * (e & 7))) : vreg[i];
     }
     __syncthreads();
-    if (kt + 1 < ntile) load_tile(kt + 1);
+    load_tile(kt + 1);  // past the last tile: clamped addresses, never stored (no branch)
+    // keep the prefetch here, ahead of this tile's products (the scheduler would otherwise
+    // sink it below them to shorten the registers' live ranges)
+    __builtin_amdgcn_sched_barrier(0);
 
     float p[2][16];
     float tmax = -INFINITY;

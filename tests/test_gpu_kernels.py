@@ -180,6 +180,7 @@ ATTN_CASES = [
     ("llada_block32_kv1024", 1, 32, 32, 32, 1024, "bf16"),
     ("llada_block32_kv2024", 1, 32, 32, 32, 2024, "bf16"),
     ("gqa_7to1_b2", 2, 28, 4, 32, 1000, "bf16"),
+    ("gqa_7to1_b8_multi_subtile", 8, 28, 4, 32, 1024, "bf16"),
     ("ragged_rows_keys", 1, 4, 2, 20, 77, "bf16"),
     ("two_row_tiles", 1, 2, 1, 64, 300, "bf16"),
     ("flash_many_rows", 1, 2, 2, 200, 333, "bf16"),
