@@ -6,8 +6,10 @@
 // models").  During a cached step the block's queries read the cached K/V of all S
 // positions (their own rows freshly written); during a refresh every row is a query.
 //
-// Cache layout: K [B][Hkv][Sp][D] and V transposed, Vt [B][Hkv][D][Sp].  With both
-// products written transposed,
+// Cache layout: K [B][Hkv][Sp][D] and V transposed in blocks of 32 keys, Vt
+// [B][Hkv][Sp/32][D][32] (vt_off): the 32 keys of a sub-tile are one contiguous 8 KB
+// block for D = 128, where a plain [D][Sp] layout spreads them over D rows Sp apart.
+// With both products written transposed,
 //     S^T = K . Q^T     (A = K rows, B = Q rows: 16-byte row loads for both)
 //     O^T = Vt . P^T    (A = Vt rows, B = P taken straight from the S^T accumulator)
 // each lane of a 32x32 MFMA tile owns one query column in both products, so the
@@ -37,10 +39,11 @@ __device__ __forceinline__ bf16x8 pack_p(const float* p, int u) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-// 8 bf16 at keys k..k+7 (k % 8 == 0) of a Vt row: one 16-byte load from a clamped
-// address (Sp % 8 == 0, so every key below S is read from its own place) ...
-__device__ __forceinline__ u32x4 load8_raw(const uint16_t* row, int k, int Sp) {
-  return *reinterpret_cast<const u32x4*>(row + min(k, Sp - 8));
+// 8 bf16 of dim d at keys k..k+7 (k % 8 == 0) of one (sequence, KV head)'s Vt: one
+// 16-byte load from a clamped key (Sp % 32 == 0, so every key below S is read from its
+// own place and the 8 keys never straddle a 32-key block) ...
+__device__ __forceinline__ u32x4 load8_raw(const uint16_t* vb, int d, int k, int Sp) {
+  return *reinterpret_cast<const u32x4*>(vb + vt_off(d, min(k, Sp - 8), HD));
 }
 // ... and, where the 8 keys may reach S, the keys >= S zeroed (n = S - k).  The mask is
 // applied where the value is used, not right after the load: masking at the load would
@@ -93,7 +96,7 @@ __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
     for (int st = 0; st < 4; ++st) t.k[tau][st] = *reinterpret_cast<const u32x4*>(kp + 32 * st);
   }
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) t.v[dt] = load8_raw(vbase + (int64_t)(16 * dt + li) * Sp, key0 + 8 * j, Sp);
+  for (int dt = 0; dt < 8; ++dt) t.v[dt] = load8_raw(vbase, 16 * dt + li, key0 + 8 * j, Sp);
 }
 
 // ONE: every wave has a single 32-key sub-tile (nsub == 1): one operand tile in
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
     for (int i = 0; i < 4; ++i) {
       const int e = threadIdx.x + 256 * i;
       const int r = e >> 3, c8 = e & 7;   // Vt: 128 rows x 8 chunks of 8 keys
-      vreg[i] = load8_raw(vb + (int64_t)r * Sp, kbase + 8 * c8, Sp);
+      vreg[i] = load8_raw(vb, r, kbase + 8 * c8, Sp);
     }
   };
   load_tile(0);
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(128) void attn_f32(const float* __restrict__ q,
   const float* vb = vt + ((int64_t)b * Hkv + hkv) * D * Sp;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float a = 0.f;
-    for (int j = 0; j < S; ++j) a += sc[j] * vb[(int64_t)d * Sp + j];
+    for (int j = 0; j < S; ++j) a += sc[j] * vb[vt_off(d, j, D)];
     o[((int64_t)b * R + row) * (Hq * D) + hq * D + d] = a / sum;
   }
 }

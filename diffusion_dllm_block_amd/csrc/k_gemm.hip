@@ -5,7 +5,8 @@
 // to one epilogue (kernels.h: EpiKind):
 //   QKV    : RoPE on q and k (rotate-half, pairs j and j + D/2, table cos/sin[pos][j]),
 //            q scattered to [B][Hq][R][D], k into the cache K [B][Hkv][Sp][D], v into the
-//            transposed cache Vt [B][Hkv][D][Sp] (the block's own K/V written in place);
+//            transposed, 32-key-blocked cache Vt (vt_off; the block's own K/V written in
+//            place);
 //   SWIGLU : a virtual tile is 64 gate rows + the matching 64 up rows of W, so the tile
 //            holds both halves of silu(gate) * up;
 //   RESID  : fp32 residual stream += tile;  F32: logits = logit_scale * tile;  STORE.
@@ -96,8 +97,8 @@ __device__ void epilogue(const float* tile, int ldt, int rows, int m0, int vc0, 
       } else {
         int h = gh - e.Hq - e.Hkv;
         T* dst = (T*)e.vtc + ((int64_t)bs * e.Hkv + h) * D * (int64_t)e.Sp;
-        Elt<T>::store(dst, (int64_t)j * e.Sp + pos, x1);
-        Elt<T>::store(dst, (int64_t)(j + half) * e.Sp + pos, x2);
+        Elt<T>::store(dst, vt_off(j, pos, D), x1);
+        Elt<T>::store(dst, vt_off(j + half, pos, D), x2);
       }
     }
   }
@@ -849,8 +850,8 @@ __device__ __forceinline__ void qkv_pair(const EpiArgs& e, int m, int hs, int d,
     dst[d + 64] = f2bf(x2 * cs + x1 * sn);
   } else {
     uint16_t* dst = (uint16_t*)e.vtc + ((int64_t)bs * e.Hkv + (hs - e.Hq - e.Hkv)) * 128 * (int64_t)e.Sp;
-    dst[(int64_t)d * e.Sp + pos] = f2bf(x1);
-    dst[(int64_t)(d + 64) * e.Sp + pos] = f2bf(x2);
+    dst[vt_off(d, pos, 128)] = f2bf(x1);
+    dst[vt_off(d + 64, pos, 128)] = f2bf(x2);
   }
 }
 

@@ -27,7 +27,7 @@ struct EpiArgs {
   // QKV
   void* qo = nullptr;              // T [B][Hq][R][D]
   void* kc = nullptr;              // T [B][Hkv][Sp][D]  (this layer's K)
-  void* vtc = nullptr;             // T [B][Hkv][D][Sp]  (this layer's V, transposed)
+  void* vtc = nullptr;             // T [B][Hkv][Sp/32][D][32]  (this layer's V, see vt_off)
   const float* rcos = nullptr;     // [S][D/2]
   const float* rsin = nullptr;
   int Hq = 0, Hkv = 0, D = 0, R = 0, pos0 = 0, Sp = 0;
@@ -38,6 +38,13 @@ struct EpiArgs {
   int rseg = 0, rd = 0;
   float reps = 0.f;
 };
+
+// The value cache holds V transposed and blocked by 32 keys: per (sequence, KV head),
+// [Sp/32][D][32], so value (dim d, key k) sits at vt_off(d, k, D) and the 32 keys x D
+// dims of one block are contiguous (Sp is a multiple of 32).
+__host__ __device__ inline int64_t vt_off(int d, int k, int D) {
+  return ((int64_t)(k >> 5) * D + d) * 32 + (k & 31);
+}
 
 enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3, GEMM_MID = 4 };
 constexpr int kSkinnyRows = 64;  // bf16 GEMMs with at most this many rows stream weights

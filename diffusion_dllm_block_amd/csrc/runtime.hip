@@ -619,8 +619,9 @@ dllm_status dllm_kernel_block_attention(const void* q, const void* k, const void
   if (B < 1 || Hq < 1 || Hkv < 1 || R < 1 || S < 1 || D < 1 || Sp < S)
     return fail(DLLM_E_SHAPE, "sizes must be positive and Sp >= S");
   if (Hq % Hkv) return fail(DLLM_E_SHAPE, "Hq %% Hkv != 0");
-  if (dtype == DLLM_BF16 && (D != 128 || Sp % 8))
-    return fail(DLLM_E_UNSUPPORTED, "bf16 attention needs D == 128 and Sp %% 8 == 0");
+  if (Sp % 32) return fail(DLLM_E_UNSUPPORTED, "Sp must be a multiple of 32 (32-key Vt blocks)");
+  if (dtype == DLLM_BF16 && D != 128)
+    return fail(DLLM_E_UNSUPPORTED, "bf16 attention needs D == 128");
   if (dtype == DLLM_F32 && (D > 128 || S > 12000))
     return fail(DLLM_E_UNSUPPORTED, "fp32 attention needs D <= 128 and S <= 12000");
   AttnPlan p;

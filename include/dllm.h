@@ -108,7 +108,9 @@ typedef struct {
  * kv_cache: device buffer of dllm_kv_cache_bytes(); layout per layer l (in elements of
  *   T, Sp = S rounded up to a multiple of 64):
  *     K  at l*2*B*Hkv*Sp*D                 : [B][Hkv][Sp][D]  (post-RoPE keys)
- *     Vt at l*2*B*Hkv*Sp*D + B*Hkv*Sp*D    : [B][Hkv][D][Sp]  (values, transposed)
+ *     Vt at l*2*B*Hkv*Sp*D + B*Hkv*Sp*D    : [B][Hkv][Sp/32][D][32]  (values, transposed
+ *        in blocks of 32 positions: value (dim d, position p) of one (sequence, KV head)
+ *        at ((p / 32) * D + d) * 32 + p % 32)
  *   positions >= S are never read.
  * workspace: device scratch of dllm_workspace_bytes(); dllm_prefill_cache initialises
  *   it and must run before the first dllm_block_step / dllm_refresh_cache.           */
@@ -195,8 +197,9 @@ size_t dllm_kernel_workspace_bytes(int32_t B, int32_t Hq, int32_t R, int32_t S, 
 
 /* Non-causal attention of R query rows per (sequence, query head) against S cached
  * keys ([A] 1.1: the block's queries read the cached KV of all positions).
- *   q  T [B][Hq][R][D];  k T [B][Hkv][Sp][D];  vt T [B][Hkv][D][Sp]  (Sp >= S; keys
- *   >= S ignored);  o T [B][R][Hq*D]  (row-major, ready for the output projection).
+ *   q  T [B][Hq][R][D];  k T [B][Hkv][Sp][D];  vt T [B][Hkv][Sp/32][D][32] (values
+ *   transposed in blocks of 32 keys, as in the KV cache; Sp >= S and a multiple of 32;
+ *   keys >= S ignored);  o T [B][R][Hq*D]  (row-major, ready for the output projection).
  *   o = softmax(q k^T / sqrt(D)) v over all S keys, fp32 softmax and accumulation.
  * Supported: DLLM_BF16 with D == 128, or DLLM_F32 with D <= 128; Hq % Hkv == 0.     */
 dllm_status dllm_kernel_block_attention(const void* q, const void* k, const void* vt, void* o,

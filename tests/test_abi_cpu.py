@@ -127,7 +127,9 @@ def test_null_descriptors(lib):
 def test_kernel_entry_validation(lib):
     f = lib.cdll.dllm_kernel_block_attention
     # bf16 needs D == 128
-    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 4, 10, 16, 64, bd.BF16, None, 0, None) == -3
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 4, 10, 32, 64, bd.BF16, None, 0, None) == -3
+    # the value cache comes in 32-key blocks: Sp must be a multiple of 32
+    assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 4, 10, 16, 128, bd.BF16, None, 0, None) == -3
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 3, 2, 4, 10, 16, 16, bd.F32, None, 0, None) == -2
     assert f(FAKE, FAKE, FAKE, FAKE, 1, 2, 2, 4, 10, 8, 16, bd.F32, None, 0, None) == -2  # Sp < S
     g = lib.cdll.dllm_kernel_confidence_unmask

@@ -156,15 +156,17 @@ def run_attn(lib, q, k, v, B, Hq, Hkv, R, S, D, dtype):
     to = dev_bf16 if dtype == "bf16" else dev_f32
     kp = np.zeros((B, Hkv, Sp, D), q.dtype)
     kp[:, :, :S] = k
-    vt = np.zeros((B, Hkv, D, Sp), q.dtype)
-    vt[:, :, :, :S] = np.swapaxes(v, -1, -2)
+    vp = np.zeros((B, Hkv, Sp, D), q.dtype)
+    vp[:, :, :S] = v
     # poison the padding: keys >= S must never be read
     if dtype == "bf16":
         kp[:, :, S:] = 0x7FC0
-        vt[:, :, :, S:] = 0x7FC0
+        vp[:, :, S:] = 0x7FC0
     else:
         kp[:, :, S:] = np.nan
-        vt[:, :, :, S:] = np.nan
+        vp[:, :, S:] = np.nan
+    # values transposed in blocks of 32 keys: [B][Hkv][Sp/32][D][32]
+    vt = np.ascontiguousarray(vp.reshape(B, Hkv, Sp // 32, 32, D).swapaxes(-1, -2))
     qd, kd, vd = to(q), to(kp), to(vt)
     o = torch.empty((B, R, Hq * D), dtype=qd.dtype, device="cuda")
     wsb = lib.raw("dllm_kernel_workspace_bytes")(B, Hq, R, S, D, 0, 0)
