@@ -116,6 +116,49 @@ __device__ __forceinline__ Trip block_merge(float m, float s, F find_idx, float*
   return r;
 }
 
+// The slice triple from values held in registers: thread tid holds ids
+// lo + (j * kConfThreads + tid) * 8 + e (j < IT, e < 8) in v[j][e]; ids past hi and the
+// mask id are dropped.  The thread's maximum first, then one exp per value against it,
+// and the argmax search only in threads that hold the slice maximum.
+template <int IT>
+__device__ __forceinline__ Trip slice_trip(float (&v)[IT][8], int lo, int hi, int mask_id,
+                                           float* rm, float* rs, int* ri) {
+  constexpr int SPAN = IT * kConfThreads * 8;
+  const int tid = threadIdx.x;
+  if (hi - lo < SPAN || (lo <= mask_id && mask_id < hi)) {  // uniform: ragged or mask slice
+#pragma unroll
+    for (int j = 0; j < IT; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = lo + (j * kConfThreads + tid) * 8 + e;
+        if (i >= hi || i == mask_id) v[j][e] = -INFINITY;
+      }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < IT; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, v[j][e]);
+  float s = 0.f;
+  if (m != -INFINITY) {
+    const float ml = m * kLog2e;
+#pragma unroll
+    for (int j = 0; j < IT; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, -ml));
+  }
+  auto find = [&](float M) {
+    int best = 0x7fffffff;
+#pragma unroll
+    for (int j = IT - 1; j >= 0; --j)
+#pragma unroll
+      for (int e = 7; e >= 0; --e)
+        if (v[j][e] == M) best = lo + (j * kConfThreads + tid) * 8 + e;
+    return best;
+  };
+  return block_merge(m, s, find, rm, rs, ri);
+}
+
 // Pass 1, one workgroup per (slice, row).  A slice is chunk consecutive ids (the last one
 // shorter).  When chunk == IT * 2048 (the usual plan) each thread holds its IT groups of 8
 // values in registers: maximum first, then one exp per value, and the argmax search only
@@ -140,38 +183,7 @@ __global__ __launch_bounds__(kConfThreads) void conf_partials_kernel(
 #pragma unroll
     for (int j = 0; j < IT; ++j)  // clamped in-row address; values past hi are dropped
       load8<T>(zr + min(lo + (j * kConfThreads + tid) * 8, V - 8), v[j]);
-    if (hi - lo < SPAN || (lo <= mask_id && mask_id < hi)) {  // uniform: ragged or mask slice
-#pragma unroll
-      for (int j = 0; j < IT; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int i = lo + (j * kConfThreads + tid) * 8 + e;
-          if (i >= hi || i == mask_id) v[j][e] = -INFINITY;
-        }
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < IT; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, v[j][e]);
-    float s = 0.f;
-    if (m != -INFINITY) {
-      const float ml = m * kLog2e;
-#pragma unroll
-      for (int j = 0; j < IT; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += __builtin_amdgcn_exp2f(fmaf(v[j][e], kLog2e, -ml));
-    }
-    auto find = [&](float M) {
-      int best = 0x7fffffff;
-#pragma unroll
-      for (int j = IT - 1; j >= 0; --j)
-#pragma unroll
-        for (int e = 7; e >= 0; --e)
-          if (v[j][e] == M) best = lo + (j * kConfThreads + tid) * 8 + e;
-      return best;
-    };
-    t = block_merge(m, s, find, rm, rs, ri);
+    t = slice_trip<IT>(v, lo, hi, mask_id, rm, rs, ri);
   } else {
     Trip u{-INFINITY, 0.f, 0x7fffffff};
     if ((V % 8) == 0) {
@@ -195,6 +207,52 @@ __global__ __launch_bounds__(kConfThreads) void conf_partials_kernel(
     }
     t = block_merge(u.m, u.s, [&](float) { return u.idx; }, rm, rs, ri);
   }
+  if (tid == 0) {
+    const int64_t o = (int64_t)row * nsplit + split;
+    pm[o] = t.m;
+    ps[o] = t.s;
+    pi[o] = t.idx;
+  }
+}
+
+// Pass 1 fused with the LM head's split-K reduction: the logits of the slice are formed
+// in registers from the weight-streaming GEMM's partials, exactly as reduce_epilogue
+// forms them (the splits summed in order, times the row's deferred RMS factor, times the
+// logit scale), stored only when the caller wants them, and reduced to the slice triple.
+// This removes the fp32 logits round trip through memory.  Needs V % 8 == 0 and
+// chunk == IT * kConfThreads * 8 (the plan's usual shape).
+template <int IT>
+__global__ __launch_bounds__(kConfThreads) void lm_conf_partials_kernel(
+    PartView pv, EpiArgs e, float* __restrict__ logits, int V, int mask_id, int nsplit,
+    int chunk, float* pm, float* ps, int* pi) {
+  __shared__ float rm[kConfThreads / kWave], rs[kConfThreads / kWave];
+  __shared__ int ri[kConfThreads / kWave];
+  const int split = blockIdx.x, row = blockIdx.y;
+  const int lo = split * chunk;
+  const int hi = min(V, lo + chunk);
+  const int tid = threadIdx.x;
+  const float r = row_rms_factor(e, row);
+  float v[IT][8];
+#pragma unroll
+  for (int j = 0; j < IT; ++j) {
+    const int c = min(lo + (j * kConfThreads + tid) * 8, V - 8);  // clamped; dropped past hi
+    const float4 a = scale4(sum_split4(pv, row, c), r);
+    const float4 b = scale4(sum_split4(pv, row, c + 4), r);
+    v[j][0] = a.x * e.scale; v[j][1] = a.y * e.scale; v[j][2] = a.z * e.scale; v[j][3] = a.w * e.scale;
+    v[j][4] = b.x * e.scale; v[j][5] = b.y * e.scale; v[j][6] = b.z * e.scale; v[j][7] = b.w * e.scale;
+  }
+  if (logits) {
+#pragma unroll
+    for (int j = 0; j < IT; ++j) {
+      const int c = lo + (j * kConfThreads + tid) * 8;
+      if (c < hi) {  // hi and c are multiples of 8: all 8 in range
+        float* o = logits + (int64_t)row * e.ldy + c;
+        *reinterpret_cast<float4*>(o) = make_float4(v[j][0], v[j][1], v[j][2], v[j][3]);
+        *reinterpret_cast<float4*>(o + 4) = make_float4(v[j][4], v[j][5], v[j][6], v[j][7]);
+      }
+    }
+  }
+  const Trip t = slice_trip<IT>(v, lo, hi, mask_id, rm, rs, ri);
   if (tid == 0) {
     const int64_t o = (int64_t)row * nsplit + split;
     pm[o] = t.m;
@@ -354,6 +412,33 @@ hipError_t launch_conf_unmask(int ldtype, const ConfPlan& p, const void* logits,
   }
 #undef DLLM_CONF_IT
 #undef DLLM_CONF
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  conf_finalize_kernel<<<B, kConfThreads, 0, st>>>(K, p.nsplit, mask_id, tau, pm, ps, pi, tokens,
+                                                   ld_tokens, conf, argmax, n_unmasked,
+                                                   remaining, unmasked_idx);
+  return hipGetLastError();
+}
+
+bool lm_conf_fusable(const ConfPlan& p, int V) {
+  return V % 8 == 0 && p.chunk == p.it * kConfThreads * 8;
+}
+
+hipError_t launch_lm_conf_unmask(const ConfPlan& p, const PartView& pv, const EpiArgs& e,
+                                 float* logits, int B, int K, int V, int mask_id, float tau,
+                                 int* tokens, int ld_tokens, float* conf, int* argmax,
+                                 int* n_unmasked, int* remaining, int* unmasked_idx, float* pm,
+                                 float* ps, int* pi, hipStream_t st) {
+  if (B <= 0 || K <= 0) return hipSuccess;
+  if (K > kWave || K * p.nsplit > kConfMaxParts || !lm_conf_fusable(p, V))
+    return hipErrorInvalidValue;
+  dim3 grid(p.nsplit, B * K);
+  switch (p.it) {
+    case 1: lm_conf_partials_kernel<1><<<grid, kConfThreads, 0, st>>>(pv, e, logits, V, mask_id, p.nsplit, p.chunk, pm, ps, pi); break;
+    case 2: lm_conf_partials_kernel<2><<<grid, kConfThreads, 0, st>>>(pv, e, logits, V, mask_id, p.nsplit, p.chunk, pm, ps, pi); break;
+    case 4: lm_conf_partials_kernel<4><<<grid, kConfThreads, 0, st>>>(pv, e, logits, V, mask_id, p.nsplit, p.chunk, pm, ps, pi); break;
+    default: lm_conf_partials_kernel<8><<<grid, kConfThreads, 0, st>>>(pv, e, logits, V, mask_id, p.nsplit, p.chunk, pm, ps, pi); break;
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   conf_finalize_kernel<<<B, kConfThreads, 0, st>>>(K, p.nsplit, mask_id, tau, pm, ps, pi, tokens,

@@ -801,39 +801,11 @@ __global__ __launch_bounds__(256) void gemm_f32(const float* __restrict__ X, int
   epilogue<float, EPI>(tile, TL, 32, m0, vc0, M, Nv, e);
 }
 
+
 // ============================================================================
 // split-K reduction + epilogue for the skinny GEMM (partials in 64-column virtual order)
 // ============================================================================
-// One thread per 4 consecutive outputs; partials summed in split order.
-__device__ __forceinline__ float4 sum_split4(const PartView& pv, int m, int c) {
-  const int64_t stride = pv.split_stride();
-  const float* p = pv.p + pv.off(m, c);
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < pv.splits; s0 += 4) {
-    float4 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = (s0 + u < pv.splits) ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
-                                  : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (s0 + u < pv.splits) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
-  }
-  return s;
-}
-
-// Deferred RMS factor of row m (1 when the input was already normalised); the segment
-// sums are added in segment order.
-__device__ __forceinline__ float row_rms_factor(const EpiArgs& e, int m) {
-  if (e.rss == nullptr) return 1.f;
-  const float* s = e.rss + (int64_t)m * e.rseg;
-  float t = 0.f;
-  for (int i = 0; i < e.rseg; ++i) t += s[i];
-  return 1.0f / sqrtf(t / (float)e.rd + e.reps);
-}
-__device__ __forceinline__ float4 scale4(float4 v, float r) {
-  return make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
-}
+// One thread per 4 consecutive outputs (helpers in kernels.h).
 
 // One RoPE pair of the QKV epilogue (head_dim 128): head slot hs (q heads, then k, then
 // v), dims d and d + 64 of row m, with the sums x1 and x2.  q and k are rotated at the

@@ -73,6 +73,40 @@ struct PartView {
   }
 };
 
+#ifdef __HIPCC__
+// Split-K sums for the reductions (reduce_epilogue, the fused LM-head confidence pass).
+// Sum of split partials at (m, c..c+3), in split order.
+__device__ __forceinline__ float4 sum_split4(const PartView& pv, int m, int c) {
+  const int64_t stride = pv.split_stride();
+  const float* p = pv.p + pv.off(m, c);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < pv.splits; s0 += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = (s0 + u < pv.splits) ? *reinterpret_cast<const float4*>(p + (s0 + u) * stride)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (s0 + u < pv.splits) { s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w; }
+  }
+  return s;
+}
+
+// Deferred RMS factor of row m (1 when the input was already normalised); the segment
+// sums are added in segment order.
+__device__ __forceinline__ float row_rms_factor(const EpiArgs& e, int m) {
+  if (e.rss == nullptr) return 1.f;
+  const float* s = e.rss + (int64_t)m * e.rseg;
+  float t = 0.f;
+  for (int i = 0; i < e.rseg; ++i) t += s[i];
+  return 1.0f / sqrtf(t / (float)e.rd + e.reps);
+}
+__device__ __forceinline__ float4 scale4(float4 v, float r) {
+  return make_float4(v.x * r, v.y * r, v.z * r, v.w * r);
+}
+#endif
+
 struct GemmPlan {
   int kind = 0;
   int mt = 1;            // skinny: 16-row MFMA tiles per workgroup (1, 2 or 4)
@@ -128,6 +162,15 @@ hipError_t launch_conf_unmask(int ldtype, const ConfPlan& p, const void* logits,
                               int V, int mask_id, float tau, int* tokens, int ld_tokens,
                               float* conf, int* argmax, int* n_unmasked, int* remaining,
                               int* unmasked_idx, float* pm, float* ps, int* pi, hipStream_t st);
+// The same with pass 1 fused into the LM head's split-K reduction (partials pv, epilogue
+// args e as for reduce_epilogue<EPI_F32>); logits (row stride e.ldy) are written only if
+// non-null.  Usable when lm_conf_fusable(p, V).
+bool lm_conf_fusable(const ConfPlan& p, int V);
+hipError_t launch_lm_conf_unmask(const ConfPlan& p, const PartView& pv, const EpiArgs& e,
+                                 float* logits, int B, int K, int V, int mask_id, float tau,
+                                 int* tokens, int ld_tokens, float* conf, int* argmax,
+                                 int* n_unmasked, int* remaining, int* unmasked_idx, float* pm,
+                                 float* ps, int* pi, hipStream_t st);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t launch_rope_table(float* cosb, float* sinb, int S, int D, float theta, hipStream_t st);

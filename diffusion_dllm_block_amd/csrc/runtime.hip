@@ -262,8 +262,18 @@ struct Ctx {
   }
 };
 
+// The split partials of a GEMM whose reduction the caller runs itself.
+struct Deferred {
+  bool on = false;
+  PartView pv;
+  EpiArgs e;
+};
+
+// One GEMM with its epilogue.  With `defer`, a weight-streaming GEMM (whose partials
+// cover every output column) leaves its reduce_epilogue to the caller: the partials and
+// the epilogue arguments (the deferred RMS factor attached) are returned in *defer.
 dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const void* W, int M,
-                 int Nv, int K, const EpiArgs& e) {
+                 int Nv, int K, const EpiArgs& e, Deferred* defer = nullptr) {
   GemmPlan p = gemm_plan(c.d.dtype, M, Nv, K, epi);
   if (p.part_floats > c.w.gpart_floats || p.counters > c.w.gcnt_n)
     return fail(DLLM_E_WORKSPACE, "internal: GEMM plan exceeds the workspace plan");
@@ -284,7 +294,11 @@ dllm_status gemm(const Ctx& c, int cls, int epi, const void* X, int ldx, const v
     HIP_TRY(launch_gemm_only(c.d.dtype, epi, p, X, ldx, W, M, Nv, K, er, c.at<float>(c.w.gpart),
                              c.at<int>(c.w.gcnt), c.st));
   }
-  if (p.reduce) {
+  if (p.reduce && defer && p.kind == GEMM_SKINNY) {  // partials cover every column
+    defer->on = true;
+    defer->pv = p.view(c.at<float>(c.w.gpart), M, Nv);
+    defer->e = er;
+  } else if (p.reduce) {
     ProfScope ps(DLLM_K_SPLIT_REDUCE, c.st);
     HIP_TRY(launch_reduce_epilogue(epi, p.view(c.at<float>(c.w.gpart), M, Nv), er, c.st));
   }
@@ -402,15 +416,25 @@ dllm_status decode_tail(const Ctx& c, int b, int R, int* n_un, int* rem, float* 
   float* lg = logits ? logits : c.at<float>(c.w.logits);
   EpiArgs el;
   el.y = lg; el.ldy = d.V; el.scale = d.lscale;
-  st = gemm(c, DLLM_K_LM_HEAD, EPI_F32, h, d.d, c.m->lm_head, d.B * d.K, d.V, d.d, el);
-  if (st) return st;
   ConfPlan cp = conf_plan(d.B * d.K, d.V, d.B);
+  // A weight-streaming LM head leaves split partials: the confidence pass sums them
+  // itself, so the fp32 logits go to memory only when the caller asked for them.
+  Deferred df;
+  st = gemm(c, DLLM_K_LM_HEAD, EPI_F32, h, d.d, c.m->lm_head, d.B * d.K, d.V, d.d, el,
+            lm_conf_fusable(cp, d.V) ? &df : nullptr);
+  if (st) return st;
   ProfScope ps(DLLM_K_CONF_UNMASK, c.st);
-  HIP_TRY(launch_conf_unmask(F32, cp, lg, d.B, d.K, d.V, d.mask, d.tau, c.s->tokens + s0, d.S,
-                             conf ? conf : c.at<float>(c.w.conf),
-                             argmax ? argmax : c.at<int>(c.w.argmax), n_un, rem, nullptr,
-                             c.at<float>(c.w.cpm), c.at<float>(c.w.cps), c.at<int>(c.w.cpi),
-                             c.st));
+  float* cf = conf ? conf : c.at<float>(c.w.conf);
+  int* am = argmax ? argmax : c.at<int>(c.w.argmax);
+  if (df.on)
+    HIP_TRY(launch_lm_conf_unmask(cp, df.pv, df.e, logits, d.B, d.K, d.V, d.mask, d.tau,
+                                  c.s->tokens + s0, d.S, cf, am, n_un, rem, nullptr,
+                                  c.at<float>(c.w.cpm), c.at<float>(c.w.cps), c.at<int>(c.w.cpi),
+                                  c.st));
+  else
+    HIP_TRY(launch_conf_unmask(F32, cp, lg, d.B, d.K, d.V, d.mask, d.tau, c.s->tokens + s0, d.S,
+                               cf, am, n_un, rem, nullptr, c.at<float>(c.w.cpm),
+                               c.at<float>(c.w.cps), c.at<int>(c.w.cpi), c.st));
   return DLLM_OK;
 }
 

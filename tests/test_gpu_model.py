@@ -176,6 +176,32 @@ def test_bf16_steps_are_deterministic(lib):
     assert np.array_equal(outs[0][1], outs[1][1])
 
 
+@pytest.mark.parametrize("entry", ["step", "refresh_step"])
+def test_decisions_without_logits_match_with_logits(lib, entry):
+    """Without a logits buffer the confidence pass sums the LM head's split partials
+    itself (no fp32 logits in memory); with one it also stores them.  The logits are the
+    same values either way, so confidence, argmax and the unmasked tokens must agree bit
+    for bit (two sessions from the same state)."""
+    wl = small_bf16(B=2, K=32)
+    model = gpu_model(lib, wl)
+    prompt = synth.make_prompt(wl)
+    outs = []
+    for want in (True, False):
+        s = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+        if entry == "step":
+            s.prefill()
+            o = s.step(0, logits=want)
+        else:
+            o = s.refresh_step(0, logits=want)
+        torch.cuda.synchronize()
+        assert (o["logits"] is not None) == want
+        outs.append([o["conf"].cpu().numpy().copy(), o["argmax"].cpu().numpy().copy(),
+                     s.tokens.cpu().numpy().copy(), o["n_unmasked"].cpu().numpy().copy()])
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
+                              b.view(np.uint32) if b.dtype == np.float32 else b)
+
+
 def test_first_step_after_refresh_matches_full_forward_bf16(lib):
     """Property (a) on the GPU path: after a refresh, the first cached step's logits equal
     the oracle's no-cache full forward of the same tokens (both cache modes)."""
