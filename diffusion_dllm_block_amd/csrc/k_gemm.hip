@@ -415,13 +415,15 @@ constexpr int BG_AB_BYTES = BG_NSTG * 2 * BG_T * BG_DK * 2;  // ring of A and B 
 constexpr int BG_TILE_BYTES = 128 * TL * 4;                 // one 128x128 quarter, fp32
 constexpr int BG_SMEM = BG_AB_BYTES > BG_TILE_BYTES ? BG_AB_BYTES : BG_TILE_BYTES;
 
+// Column tiles tn0 + blockIdx.x.  With splits > 1 the tile's K piece is stored as fp32
+// partials [split][M][Nv - vbase] at column vc - vbase.
 template <int EPI, int DK, int NSTG>
 __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv, int K,
-    int kchunk, int splits, float* part, EpiArgs e) {
+    int kchunk, int splits, float* part, EpiArgs e, int tn0, int vbase) {
   extern __shared__ __attribute__((aligned(16))) unsigned char bg_smem[];
   float* tile = reinterpret_cast<float*>(bg_smem);
-  const int tn = blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
+  const int tn = tn0 + blockIdx.x, tm = blockIdx.y, split = blockIdx.z;
   const int m0 = tm * BG_T, vc0 = tn * BG_T;
   const int tid = threadIdx.x;
   // wave w: rows 128 (w & 1) .. +128, columns 64 (w >> 1) .. +64
@@ -547,11 +549,13 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
     if (splits == 1) {
       epilogue<uint16_t, EPI>(tile, TL, 128, pm0, pvc0, M, Nv, e);
     } else {
-      // residual GEMM split over K: partials summed by the next RMSNorm in split order
+      // split over K: partials summed in split order by the next RMSNorm (residual
+      // GEMMs) or by reduce_epilogue (a split tail of tiles)
+      const int Np = Nv - vbase;
       for (int i = tid; i < 128 * 128; i += BG_THREADS) {
         const int r = i >> 7, c = i & 127;
         const int m = pm0 + r, vc = pvc0 + c;
-        if (m < M && vc < Nv) part[((int64_t)split * M + m) * Nv + vc] = tile[r * TL + c];
+        if (m < M && vc < Nv) part[((int64_t)split * M + m) * Np + (vc - vbase)] = tile[r * TL + c];
       }
     }
     __syncthreads();
@@ -581,6 +585,7 @@ constexpr int MD_STG = MD_A + MD_BN * MD_DK * 2;
 constexpr int MD_SMEM = MD_NSTG * MD_STG;   // 144 KB
 constexpr int MD_TL = 132;                  // row stride (floats) of the epilogue tile
 static_assert(kMidRows * MD_TL * 4 <= MD_SMEM, "epilogue tile fits in the operand ring");
+static_assert(BG_T == kBigTile, "large tile edge");
 
 // Epilogue of a whole tile in LDS (rows 0..255, tile-local virtual columns 0..127 at
 // vc0) in wrow_s2's virtual order.  Only STORE, F32 and SWIGLU tiles are whole.
@@ -828,9 +833,10 @@ __device__ __forceinline__ void qkv_pair(const EpiArgs& e, int m, int hs, int d,
 }
 
 // Split-K reduction + epilogue over the partial columns [0, pv.N), i.e. the virtual
-// output columns [pv.vbase, pv.vbase + pv.N), in the 64-column virtual order of
-// wrow_s2 (SwiGLU: 32 gate columns then the matching 32 up columns; QKV: one head slot
-// per 128 columns, dims 0..31, 64..95, 32..63, 96..127).
+// output columns [pv.vbase, pv.vbase + pv.N), in the producing GEMM's virtual order
+// (pv.order): the 64-column order of wrow_s2 (SwiGLU: 32 gate columns then the matching
+// 32 up columns; QKV: one head slot per 128 columns, dims 0..31, 64..95, 32..63,
+// 96..127) or the large tiles' 128-column order of wrow_of (64 + 64; dims in order).
 template <int EPI>
 __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
   const int M = pv.M, Nt = pv.N;
@@ -849,13 +855,15 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
     // output column c of the span: gate at partial column 64(c/32) + c%32, up 32 further
+    // (128-column order: 128(c/64) + c%64, up 64 further)
     const int nout = Nt / 2;
     if (i4 >= (int64_t)M * nout) return;
     const int m = (int)(i4 / nout), c = (int)(i4 % nout);
-    const int vg = 64 * (c >> 5) + (c & 31);
+    const int gw = pv.order ? 64 : 32;
+    const int vg = 2 * gw * (c / gw) + (c % gw);
     const float r = row_rms_factor(e, m);
     const float4 gt = scale4(sum_split4(pv, m, vg), r);
-    const float4 up = scale4(sum_split4(pv, m, vg + 32), r);
+    const float4 up = scale4(sum_split4(pv, m, vg + gw), r);
     uint16_t* y = (uint16_t*)e.y + (int64_t)m * e.F + pv.vbase / 2 + c;
     y[0] = swiglu_bf16(gt.x, up.x); y[1] = swiglu_bf16(gt.y, up.y);
     y[2] = swiglu_bf16(gt.z, up.z); y[3] = swiglu_bf16(gt.w, up.w);
@@ -866,10 +874,13 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     const int m = (int)(i4 / (nslot * 64));
     const int rem = (int)(i4 % (nslot * 64));
     const int hl = rem / 64, d = rem % 64;
-    const int c = 64 * (2 * hl + (d >> 5)) + (d & 31);
+    // the pair (d, d + 64) of head slot hl: 64-column order keeps dims 0-31, 64-95,
+    // 32-63, 96-127; 128-column order keeps them in place
+    const int c = pv.order ? 128 * hl + d : 64 * (2 * hl + (d >> 5)) + (d & 31);
+    const int cb = pv.order ? c + 64 : c + 32;
     const float r = row_rms_factor(e, m);
     const float4 a = scale4(sum_split4(pv, m, c), r);
-    const float4 b = scale4(sum_split4(pv, m, c + 32), r);
+    const float4 b = scale4(sum_split4(pv, m, cb), r);
     const int hs = pv.vbase / 128 + hl;
     qkv_pair(e, m, hs, d + 0, a.x, b.x);
     qkv_pair(e, m, hs, d + 1, a.y, b.y);
@@ -985,6 +996,31 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   // 256 <= M < 512 (one row tile of 256): the large tile reads each weight tile once,
   // while the 128-row tiles read it twice; worth it once it fills a round of CUs
   const bool big_mid = M >= 256 && M < 512 && big_tiles >= 256;
+  // Non-residual GEMMs whose ragged last round of large tiles is made of whole column
+  // tiles: those columns are split over K into about one round of pieces (partials,
+  // reduce_epilogue), the rest run as whole tiles (e.g. the 2024-row QKV: 256 whole tiles
+  // and 16 column tiles x 8 row tiles in 2 K halves, 1.5 rounds instead of 2).
+  if (K % TB_K == 0 && M >= 512 && epi != EPI_RESID) {
+    const int P = num_cus();
+    const int ntn = (Nv + BG_T - 1) / BG_T, ntm = (M + BG_T - 1) / BG_T;
+    const int tail = (ntn * ntm) % P;
+    const int S = tail ? std::min(P / tail, K / TB_K) : 0;
+    // the reduction reads float4 columns and, for QKV, whole head slots
+    if (ntn * ntm > P && tail % ntm == 0 && S >= 2 && Nv % 4 == 0 &&
+        (epi != EPI_QKV || Nv % 128 == 0)) {
+      p.kind = GEMM_BIG;
+      p.ntn = ntn;
+      p.ntm = ntm;
+      p.ndp = ntn - tail / ntm;
+      const int per = (K + S - 1) / S;
+      p.kchunk = (per + TB_K - 1) / TB_K * TB_K;
+      p.splits = (K + p.kchunk - 1) / p.kchunk;
+      p.part_floats = (size_t)p.splits * M * (Nv - p.ndp * BG_T);
+      p.deferred = true;
+      p.reduce = true;
+      return p;
+    }
+  }
   if (K % TB_K == 0 && ((M >= 512 && big_fills) || big_mid)) {
     p.kind = GEMM_BIG;
     p.ntn = (Nv + BG_T - 1) / BG_T;
@@ -1090,8 +1126,19 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
       if (err != hipSuccess) return err;
       attr_set = true;
     }
-    gemm_big_bf16<EPI, BG_DK, BG_NSTG><<<dim3(p.ntn, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
-        (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e);
+    if (p.ndp > 0) {  // whole column tiles [0, ndp), then the split tail
+      gemm_big_bf16<EPI, BG_DK, BG_NSTG><<<dim3(p.ndp, p.ntm, 1), BG_THREADS, BG_SMEM, st>>>(
+          (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, K, 1, part, e, 0, 0);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      gemm_big_bf16<EPI, BG_DK, BG_NSTG>
+          <<<dim3(p.ntn - p.ndp, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
+              (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e,
+              p.ndp, p.ndp * BG_T);
+    } else {
+      gemm_big_bf16<EPI, BG_DK, BG_NSTG><<<dim3(p.ntn, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
+          (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e, 0, 0);
+    }
   } else {
     gemm_tiled_bf16<EPI><<<dim3(p.ntm, p.ntn, p.splits), 256, 0, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, counters,

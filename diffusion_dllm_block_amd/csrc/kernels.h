@@ -49,6 +49,7 @@ __host__ __device__ inline int64_t vt_off(int d, int k, int D) {
 enum GemmKind { GEMM_F32 = 0, GEMM_SKINNY = 1, GEMM_TILED = 2, GEMM_BIG = 3, GEMM_MID = 4 };
 constexpr int kSkinnyRows = 64;  // bf16 GEMMs with at most this many rows stream weights
 constexpr int kMidRows = 256;    // above kSkinnyRows and up to this many: one 256-row tile
+constexpr int kBigTile = 256;    // output tile edge of the large-tile GEMM
 
 // Where split-K partial sums live.  Plain: [split][M][N].  Blocked (skinny GEMM): per split,
 // per 16-column group, one block of mrows x 16 floats in which row m, column c sits at
@@ -63,6 +64,10 @@ struct PartView {
   int mrows = 0;        // blocked: rows per block (16, 32 or 64)
   int M = 0, N = 0;     // plain: row stride is N
   int vbase = 0;        // a multiple of 128
+  // virtual column order of the producing GEMM: 0 = 64-column groups (weight-streaming and
+  // mid-size GEMMs: SwiGLU 32 gate + 32 up, QKV head dims 0-31, 64-95, 32-63, 96-127);
+  // 1 = 128-column groups (large tiles: SwiGLU 64 gate + 64 up, QKV dims in order)
+  int order = 0;
   __host__ __device__ int64_t split_stride() const {
     return blocked ? (int64_t)((N + 15) / 16) * mrows * 16 : (int64_t)M * N;
   }
@@ -116,14 +121,16 @@ struct GemmPlan {
   int counters = 0;        // split-K arrival counters
   bool deferred = false;   // residual partials left for the next RMSNorm to add
   bool reduce = false;     // a reduce_epilogue launch finishes the split columns
-  int ndp = 0;             // mid: leading tiles computed whole (direct epilogue)
+  int ndp = 0;             // mid: leading tiles computed whole (direct epilogue); large
+                           // tiles: leading column tiles computed whole, the rest split
   int units = 0;           // mid: work units (whole tiles, then tile x K-split pieces)
   PartView view(const float* part, int M, int N) const {
     PartView v;
     v.p = part; v.splits = splits; v.M = M;
     v.blocked = (kind == GEMM_SKINNY);
     v.mrows = mt * 16;
-    v.vbase = (kind == GEMM_MID) ? ndp * 128 : 0;
+    v.vbase = (kind == GEMM_MID) ? ndp * 128 : (kind == GEMM_BIG ? ndp * kBigTile : 0);
+    v.order = (kind == GEMM_BIG) ? 1 : 0;
     v.N = N - v.vbase;
     return v;
   }

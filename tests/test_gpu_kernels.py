@@ -242,6 +242,8 @@ GEMM_CASES = [
     ("mid_m130_rounds_and_tail", 130, 66624, 256, "bf16"),
     ("big_m600_ragged_splitk", 600, 640, 512, "bf16"),
     ("big_m1064_two_row_tiles", 1064, 768, 1024, "bf16"),
+    # 72 x 4 large tiles: 256 whole tiles, then 8 column tiles x 4 row tiles in 8 K pieces
+    ("big_m800_whole_and_split_tail", 800, 18400, 512, "bf16"),
     ("f32_small", 20, 200, 64, "f32"),
 ]
 
