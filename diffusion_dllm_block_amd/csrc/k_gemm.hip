@@ -272,7 +272,7 @@ constexpr int TB_SMEM = TB_AB_BYTES > TB_TILE_BYTES ? TB_AB_BYTES : TB_TILE_BYTE
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv, int K,
-    int kchunk, int splits, float* part, int* counters, EpiArgs e) {
+    int kchunk, int splits, float* part, int* counters, EpiArgs e, int tn0) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[TB_SMEM];
   __shared__ int flag;
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
   float* tile = reinterpret_cast<float*>(smem);
   // row tiles fastest: the row tiles of one weight tile are dispatched together, so the
   // weight tile streams from HBM once and the others find it in the Infinity Cache
-  const int tm = blockIdx.x, tn = blockIdx.y, split = blockIdx.z;
+  const int tm = blockIdx.x, tn = tn0 + blockIdx.y, split = blockIdx.z;
   const int m0 = tm * 128, vc0 = tn * 128;
   const int tid = threadIdx.x;
   const int w = tid >> 6, wm = w >> 1, wn = w & 1, l = tid & 63, lr = l & 31, g = l >> 5;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tiled_bf16(
     int m = m0 + r, vc = vc0 + c;
     if (m < M && vc < Nv) st_dev(&part[((int64_t)split * M + m) * Nv + vc], tile[r * TL + c]);
   }
-  if (!arrive_last(&counters[tm * gridDim.y + tn], splits, &flag)) return;
+  if (!arrive_last(&counters[tm * gridDim.y + blockIdx.y], splits, &flag)) return;
   gather_partials(tile, TL, 128, m0, vc0, M, Nv, splits, part);
   __syncthreads();
   epilogue<uint16_t, EPI>(tile, TL, 128, m0, vc0, M, Nv, e);
@@ -997,15 +997,28 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   // while the 128-row tiles read it twice; worth it once it fills a round of CUs
   const bool big_mid = M >= 256 && M < 512 && big_tiles >= 256;
   // Non-residual GEMMs whose ragged last round of large tiles is made of whole column
-  // tiles: those columns are split over K into about one round of pieces (partials,
-  // reduce_epilogue), the rest run as whole tiles (e.g. the 2024-row QKV: 256 whole tiles
-  // and 16 column tiles x 8 row tiles in 2 K halves, 1.5 rounds instead of 2).
+  // tiles: the leading columns run as whole tiles, and the trailing ones either as
+  // 128x128 tiles when those fill a round of CUs (e.g. the 2024-row QKV: 256 large tiles,
+  // then 16 x 2 columns x 16 rows of small tiles), or split over K into about one round of
+  // large-tile pieces (partials, reduce_epilogue).
   if (K % TB_K == 0 && M >= 512 && epi != EPI_RESID) {
     const int P = num_cus();
     const int ntn = (Nv + BG_T - 1) / BG_T, ntm = (M + BG_T - 1) / BG_T;
     const int tail = (ntn * ntm) % P;
     const int S = tail ? std::min(P / tail, K / TB_K) : 0;
     // the reduction reads float4 columns and, for QKV, whole head slots
+    if (ntn * ntm > P && tail % ntm == 0 && 4 * tail >= P) {
+      // the tail's columns as 128x128 tiles (4 per large tile) fill a round of CUs: run
+      // them on the tiled kernel, whole K, epilogue in place (no partials)
+      p.kind = GEMM_BIG;
+      p.ntn = ntn;
+      p.ntm = ntm;
+      p.ndp = ntn - tail / ntm;
+      p.tail_tiled = true;
+      p.kchunk = K;
+      p.splits = 1;
+      return p;
+    }
     if (ntn * ntm > P && tail % ntm == 0 && S >= 2 && Nv % 4 == 0 &&
         (epi != EPI_QKV || Nv % 128 == 0)) {
       p.kind = GEMM_BIG;
@@ -1131,6 +1144,12 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
           (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, K, 1, part, e, 0, 0);
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
+      if (p.tail_tiled) {
+        const int tn0 = p.ndp * (BG_T / 128);
+        gemm_tiled_bf16<EPI><<<dim3((M + 127) / 128, (Nv + 127) / 128 - tn0, 1), 256, 0, st>>>(
+            (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, K, 1, part, counters, e, tn0);
+        return hipGetLastError();
+      }
       gemm_big_bf16<EPI, BG_DK, BG_NSTG>
           <<<dim3(p.ntn - p.ndp, p.ntm, p.splits), BG_THREADS, BG_SMEM, st>>>(
               (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, e,
@@ -1142,7 +1161,7 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
   } else {
     gemm_tiled_bf16<EPI><<<dim3(p.ntm, p.ntn, p.splits), 256, 0, st>>>(
         (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.kchunk, p.splits, part, counters,
-        e);
+        e, 0);
   }
   return hipGetLastError();
 }

@@ -124,6 +124,7 @@ struct GemmPlan {
   int ndp = 0;             // mid: leading tiles computed whole (direct epilogue); large
                            // tiles: leading column tiles computed whole, the rest split
   int units = 0;           // mid: work units (whole tiles, then tile x K-split pieces)
+  bool tail_tiled = false; // large tiles: columns from ndp on run as 128x128 tiles
   PartView view(const float* part, int M, int N) const {
     PartView v;
     v.p = part; v.splits = splits; v.M = M;
