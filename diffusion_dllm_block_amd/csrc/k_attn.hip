@@ -404,6 +404,8 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
     // sink it below them to shorten the registers' live ranges)
     __builtin_amdgcn_sched_barrier(0);
 
+    // raw scores; keys >= S (only in the last tile: a uniform test) count as -inf
+    const bool full = kbase + FK <= S;
     float p[2][16];
     float tmax = -INFINITY;
 #pragma unroll
@@ -414,14 +416,24 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
         u32x4 kv = *reinterpret_cast<const u32x4*>(&Ks[(st * 32 + lr) * KS_LD + 16 * t + 8 * g]);
         s = mfma32(as_bf16x8(kv), as_bf16x8(qf[t]), s);
       }
+      if (full) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = (kbase + st * 32 + acc_row(v, g) < S) ? s[v] * scale_log2 : -INFINITY;
-        p[st][v] = x;
-        tmax = fmaxf(tmax, x);
+        for (int v = 0; v < 16; ++v) {
+          p[st][v] = s[v];
+          tmax = fmaxf(tmax, s[v]);
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float x = (kbase + st * 32 + acc_row(v, g) < S) ? s[v] : -INFINITY;
+          p[st][v] = x;
+          tmax = fmaxf(tmax, x);
+        }
       }
     }
-    tmax = xor32_combine(tmax, fmax_op);
+    // the scale is positive, so the scaled maximum is the maximum of the scaled scores;
+    // exp2(score * scale - max) is one FMA per score
+    tmax = xor32_combine(tmax, fmax_op) * scale_log2;
     const float m_new = fmaxf(m_run, tmax);   // finite: every tile has a valid key
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     float ls = 0.f;
@@ -429,14 +441,18 @@ __global__ __launch_bounds__(256, 2) void attn_flash_bf16(
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        p[st][v] = __builtin_amdgcn_exp2f(p[st][v] - m_new);
+        p[st][v] = __builtin_amdgcn_exp2f(fmaf(p[st][v], scale_log2, -m_new));
         ls += p[st][v];
       }
     ls = xor32_combine(ls, add_op);
     l_run = l_run * alpha + ls;
     m_run = m_new;
+    // alpha is exactly 1 where the running maximum did not move: rescale only if some
+    // lane's did (a uniform branch)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+    }
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
