@@ -16,8 +16,14 @@ diffusion models", steps 1 and 2; ccyt168.com Fast-dLLM article, sections 1.1-1.
   already complete gets no forced unmask (reading; the pages use batch 1);
 * all G tokens are generated: no end-of-sequence handling (reading).
 
-``Session`` exposes the same four operations as the GPU library (prefill, refresh,
-step, generate) so tests can drive both sides from one token state.
+Pins (tests/test_oracle_staleness.py): the cosine against its closed forms and scipy;
+the statistics on a hand-built cache; the reused positions of both cache modes by hand;
+every cosine is 1 right after a refresh, and layer 0 stays 1 after block-only token
+changes while deeper layers move.
+
+``Session`` exposes the same operations as the GPU library (prefill, refresh, step,
+generate, and the staleness measure of the cache) so tests can drive both sides from
+one token state.
 """
 from __future__ import annotations
 
@@ -66,6 +72,29 @@ class Session:
         return {"logits": logits, "conf": conf, "argmax": arg, "U": U,
                 "n_unmasked": n_un, "remaining": rem}
 
+    def reused_positions(self, b: int) -> np.ndarray:
+        """Boolean [S]: the positions whose K/V a cached step of block b reads from the
+        cache (DualCache: every position but the block's; prefix mode: those before it)."""
+        s0, s1 = self.block_span(b)
+        keep = np.zeros(self.S, dtype=bool)
+        keep[:s0] = True
+        if self.mode == "dual":
+            keep[s1:] = True
+        return keep
+
+    def staleness(self, b: int):
+        """How far the cache is from the exact K/V of the current tokens, at the positions
+        a cached step of block b would take from it.  The pages justify the cache by the
+        near-1 cosine similarity of K/V between adjacent denoising steps (ccyt168.com
+        Fast-dLLM article, section 1.1, Figure 2; techwalker.com explainer, "Core
+        innovation"); this measures that similarity for the live cache: a full forward
+        over the current tokens gives the exact K/V, compared per layer by
+        ``kv_cosine_stats``.  Returns ([L, 2 (K, V), 2 (mean, min)], reuse ratio), the
+        ratio being the fraction of the S positions read from the cache."""
+        fresh, _ = full_forward(self.M, self.tokens, logit_rows=None)
+        keep = self.reused_positions(b)
+        return kv_cosine_stats(self.cache, fresh, keep), keep.sum() / self.S
+
     def block_done(self, b: int) -> bool:
         s0, s1 = self.block_span(b)
         return not (self.tokens[:, s0:s1] == self.M.m.mask_id).any()
@@ -89,6 +118,38 @@ class Session:
         stats = {"steps": int(sum(steps_per_block)), "refreshes": refreshes,
                  "steps_per_block": steps_per_block, "tokens": self.B * self.G}
         return self.tokens[:, self.P:].copy(), stats
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Cosine similarity of the vectors along the last axis, in fp64.  Two zero vectors
+    count as identical (1), a zero and a non-zero vector as unrelated (0) (reading: the
+    pages do not meet the case)."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    dot = np.sum(a * b, axis=-1)
+    na = np.sum(a * a, axis=-1)
+    nb = np.sum(b * b, axis=-1)
+    both = (na == 0) & (nb == 0)
+    one = (na == 0) ^ (nb == 0)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        c = dot / np.sqrt(na * nb)
+    return np.where(both, 1.0, np.where(one, 0.0, c))
+
+
+def kv_cosine_stats(cached: KVCache, fresh: KVCache, keep: np.ndarray) -> np.ndarray:
+    """Per layer, for K and for V: the mean and the minimum, over every (sequence, KV
+    head, position p with keep[p]), of the cosine similarity of the cached and the fresh
+    D-vector.  [L, 2, 2]; a layer with no kept position reports (1, 1)."""
+    L = len(cached.K)
+    out = np.ones((L, 2, 2))
+    keep = np.asarray(keep, dtype=bool)
+    if not keep.any():
+        return out
+    for l in range(L):
+        for j, (a, f) in enumerate(((cached.K[l], fresh.K[l]), (cached.V[l], fresh.V[l]))):
+            c = cosine(a[:, :, keep, :], f[:, :, keep, :])
+            out[l, j] = c.mean(), c.min()
+    return out
 
 
 def generate(M: OracleModel, prompt: np.ndarray, gen_len: int, block_len: int, tau: float,
