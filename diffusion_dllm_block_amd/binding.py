@@ -65,6 +65,8 @@ _SIGS = {
     "dllm_kv_cache_bytes": (C.c_size_t, [C.POINTER(ModelDesc), C.POINTER(SeqDesc)]),
     "dllm_prefill_cache": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _P]),
     "dllm_refresh_cache": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P]),
+    "dllm_cache_staleness": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, C.c_size_t,
+                                  _P, _P]),
     "dllm_block_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P, _P]),
     "dllm_refresh_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P,
                                _P]),

@@ -418,4 +418,94 @@ hipError_t launch_synth_fill(void* dst, int64_t n, int dtype, uint64_t seed, uin
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ cache staleness
+// How far the block-wise approximate cache is from the exact K/V of the current tokens:
+// the pages report that the K/V activations of adjacent denoising steps have a cosine
+// similarity close to 1, which is what makes reusing them safe (ccyt168.com Fast-dLLM
+// article, section 1.1, the similarity check; techwalker.com explainer, "Core
+// innovation").  Pass 1, grid (B*Hkv, 2, L): one (sequence, KV head) of one layer's K
+// (y = 0) or V (y = 1); wave w takes positions w, w + 4, ... outside [x0, x1), the
+// cosine similarity of the cached and fresh D-vectors in fp32 (both zero: 1, one zero:
+// 0), summed in double and minimised per wave, then over the 4 waves in order.
+template <typename T>
+__global__ __launch_bounds__(256) void staleness_partials_kernel(
+    const T* __restrict__ cached, const T* __restrict__ fresh, int B, int Hkv, int S, int Sp,
+    int D, int x0, int x1, double* part) {
+  __shared__ double rsum[4], rcnt[4];
+  __shared__ float rmin[4];
+  const int bh = blockIdx.x, kv = blockIdx.y, l = blockIdx.z;
+  const int64_t per = (int64_t)B * Hkv * Sp * D;  // elements of K (= of Vt) per layer
+  const int64_t base = (int64_t)l * 2 * per + kv * per + (int64_t)bh * Sp * D;
+  const T* a = cached + base;
+  const T* f = fresh + base;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double sum = 0.0, cnt = 0.0;
+  float mn = INFINITY;
+  for (int p = w; p < S; p += 4) {
+    if (p >= x0 && p < x1) continue;  // uniform over the wave
+    float dot = 0.f, na = 0.f, nb = 0.f;
+    for (int d = lane; d < D; d += kWave) {
+      const int64_t o = kv == 0 ? (int64_t)p * D + d : vt_off(d, p, D);
+      const float u = Elt<T>::load(a, o), v = Elt<T>::load(f, o);
+      dot += u * v;
+      na += u * u;
+      nb += v * v;
+    }
+    dot = wave_sum_dpp(dot);
+    na = wave_sum_dpp(na);
+    nb = wave_sum_dpp(nb);
+    const float c = (na == 0.f && nb == 0.f) ? 1.f
+                    : (na == 0.f || nb == 0.f) ? 0.f
+                    : dot / sqrtf(na * nb);
+    sum += c;
+    cnt += 1.0;
+    mn = fminf(mn, c);
+  }
+  if (lane == 0) { rsum[w] = sum; rcnt[w] = cnt; rmin[w] = mn; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double s = 0.0, n = 0.0;
+    float m = INFINITY;
+    for (int i = 0; i < 4; ++i) { s += rsum[i]; n += rcnt[i]; m = fminf(m, rmin[i]); }
+    double* o = part + ((int64_t)(l * 2 + kv) * gridDim.x + bh) * 3;
+    o[0] = s;
+    o[1] = n;
+    o[2] = (double)m;
+  }
+}
+
+// Pass 2, one thread per (layer, K or V): the (sequence, head) partials in order; out
+// [L][2][2] = mean, min (1, 1 when no position is compared).
+__global__ void staleness_final_kernel(const double* part, int nbh, int n, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const double* p = part + (int64_t)i * nbh * 3;
+  double s = 0.0, c = 0.0, m = INFINITY;
+  for (int j = 0; j < nbh; ++j) {
+    s += p[3 * j];
+    c += p[3 * j + 1];
+    m = fmin(m, p[3 * j + 2]);
+  }
+  out[2 * i] = c > 0.0 ? (float)(s / c) : 1.f;
+  out[2 * i + 1] = c > 0.0 ? (float)m : 1.f;
+}
+
+hipError_t launch_staleness(int dtype, const void* cached, const void* fresh, int L, int B,
+                            int Hkv, int S, int Sp, int D, int x0, int x1, double* part,
+                            float* out, hipStream_t st) {
+  if (L <= 0 || B <= 0 || Hkv <= 0) return hipSuccess;
+  const dim3 grid(B * Hkv, 2, L);
+  if (dtype == F32)
+    staleness_partials_kernel<float><<<grid, 256, 0, st>>>((const float*)cached, (const float*)fresh,
+                                                           B, Hkv, S, Sp, D, x0, x1, part);
+  else
+    staleness_partials_kernel<uint16_t><<<grid, 256, 0, st>>>(
+        (const uint16_t*)cached, (const uint16_t*)fresh, B, Hkv, S, Sp, D, x0, x1, part);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n = L * 2;
+  staleness_final_kernel<<<(n + 63) / 64, 64, 0, st>>>(part, B * Hkv, n, out);
+  return hipGetLastError();
+}
+
 }  // namespace dllm

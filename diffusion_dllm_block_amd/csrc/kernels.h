@@ -201,6 +201,11 @@ hipError_t launch_fold_scale(int dtype, float* x, int rows, int Rin, int Kout, c
 // y[m][c] += sum over splits of the partials at (m, c), in split order (y is [M][N] fp32)
 hipError_t launch_fold_partials(float* y, const PartView& pv, hipStream_t st);
 hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st);
+// Cosine similarity of cached and fresh K/V per layer (positions outside [x0, x1)):
+// out [L][2][2] = {K mean, K min}, {V mean, V min}; part: L * 2 * B * Hkv * 3 doubles.
+hipError_t launch_staleness(int dtype, const void* cached, const void* fresh, int L, int B,
+                            int Hkv, int S, int Sp, int D, int x0, int x1, double* part,
+                            float* out, hipStream_t st);
 hipError_t launch_synth_fill(void* dst, int64_t n, int dtype, uint64_t seed, uint32_t tid,
                              double stdv, int mode, hipStream_t st);
 

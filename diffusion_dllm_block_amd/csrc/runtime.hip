@@ -530,6 +530,38 @@ dllm_status dllm_refresh_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
   return do_refresh(c);
 }
 
+dllm_status dllm_cache_staleness(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
+                                 void* fresh_cache, size_t fresh_bytes, float* out,
+                                 dllm_stream_t stream) {
+  Dims d;
+  Ws w;
+  dllm_status st = setup(m, s, &d, &w);
+  if (st) return st;
+  if (block < 0 || block >= d.nblocks) return fail(DLLM_E_STATE, "block %d outside [0, %d)", block, d.nblocks);
+  if (d.mode == DLLM_CACHE_NONE) return fail(DLLM_E_STATE, "no cache to compare in this mode");
+  if (!fresh_cache || !out) return fail(DLLM_E_NULL, "fresh_cache/out is NULL");
+  if (fresh_bytes < cache_bytes(d))
+    return fail(DLLM_E_WORKSPACE, "fresh_bytes %zu < %zu", fresh_bytes, cache_bytes(d));
+  // the per-(layer, K/V, sequence, head) partials go to the logits buffer, idle here
+  const size_t part = (size_t)d.L * 2 * d.B * d.Hkv * 3 * sizeof(double);
+  if (part > (size_t)d.B * d.K * d.V * 4)
+    return fail(DLLM_E_UNSUPPORTED, "staleness partials exceed the logits buffer");
+  // the exact K/V of the current tokens: a full forward into the fresh buffer
+  dllm_seq_desc fs = *s;
+  fs.kv_cache = fresh_cache;
+  fs.kv_cache_bytes = fresh_bytes;
+  const Ctx cf{d, m, &fs, w, (char*)s->workspace, (hipStream_t)stream};
+  st = do_refresh(cf);
+  if (st) return st;
+  // the positions the next cached step of `block` takes from the cache: every one but
+  // the block's (DualCache), those before the block (prefix)
+  const int s0 = d.P + block * d.K;
+  const int x1 = (d.mode == DLLM_CACHE_PREFIX) ? d.S : s0 + d.K;
+  HIP_TRY(launch_staleness(d.dtype, s->kv_cache, fresh_cache, d.L, d.B, d.Hkv, d.S, d.Sp, d.D,
+                           s0, x1, cf.at<double>(w.logits), out, (hipStream_t)stream));
+  return DLLM_OK;
+}
+
 dllm_status dllm_block_step(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
                             dllm_stream_t stream, int32_t* d_n_unmasked, int32_t* d_remaining,
                             float* d_logits, float* d_conf, int32_t* d_argmax) {

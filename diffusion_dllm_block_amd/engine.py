@@ -139,6 +139,25 @@ class Session:
         (dllm_refresh_step)."""
         return self._decode("dllm_refresh_step", block, logits, stream)
 
+    def staleness(self, block: int, stream=None) -> dict:
+        """Cosine similarity of the cached K/V that a cached step of `block` would read now
+        and the exact K/V of the current tokens (dllm_cache_staleness): per layer, the
+        mean and minimum over the positions taken from the cache, for K and V; and the
+        reuse ratio, the fraction of the S positions whose K/V the step takes from the
+        cache (DualCache: all but the block's; prefix mode: those before the block)."""
+        torch = _torch()
+        dev = self.tokens.device
+        fresh = torch.empty_like(self.cache)
+        out = torch.empty((self.model.shape.n_layers, 2, 2), dtype=torch.float32, device=dev)
+        self.lib.call("dllm_cache_staleness", *self._args(), block, bd.ptr(fresh),
+                      fresh.numel(), bd.ptr(out), bd.stream_handle(stream))
+        torch.cuda.synchronize(dev)
+        o = out.cpu().numpy()
+        s0 = self.P + block * self.K
+        reused = (self.S - self.K) if self.mode == bd.CACHE_DUAL else s0
+        return {"k_mean": o[:, 0, 0], "k_min": o[:, 0, 1], "v_mean": o[:, 1, 0],
+                "v_min": o[:, 1, 1], "reuse": reused / self.S}
+
     def _decode(self, entry: str, block: int, logits: bool, stream) -> dict:
         torch = _torch()
         dev = self.tokens.device

@@ -186,6 +186,23 @@ dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, 
 dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s,
                           dllm_stream_t stream, dllm_stats* out);
 
+/* Cache staleness: how far the block-wise approximate cache is from the exact K/V of
+ * the current tokens.  [A] 1.1 checks that the K/V activations of adjacent steps have a
+ * cosine similarity close to 1 and [B] "Core innovation" shows the same similarity;
+ * this measures it for the cache a cached step of `block` would read now.  A full
+ * forward of the current tokens writes the exact K/V into fresh_cache (caller-owned,
+ * dllm_kv_cache_bytes() bytes, the kv_cache layout); then, per layer and for K and V,
+ * the cosine similarity of the cached and the fresh D-vector of every (sequence, KV
+ * head, position) the step takes from the cache (DualCache: every position outside the
+ * block; prefix mode: the positions before it), averaged and minimised.  A vector pair
+ * with both norms zero counts 1, with one zero norm 0.
+ *   out: device float [n_layers][2][2] = {K mean, K min}, {V mean, V min}.
+ * tokens and kv_cache are not modified; the workspace is (as by any step).  Needs a
+ * cache mode other than DLLM_CACHE_NONE and a prior dllm_prefill_cache.             */
+dllm_status dllm_cache_staleness(const dllm_model_desc* m, const dllm_seq_desc* s,
+                                 int32_t block, void* fresh_cache, size_t fresh_bytes,
+                                 float* out, dllm_stream_t stream);
+
 /* ---- kernel-level entries (single stages on caller buffers) ---------------------- */
 
 /* Workspace needed by the two kernel-level calls below: the attention part for

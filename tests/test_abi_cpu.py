@@ -118,6 +118,20 @@ def test_small_buffers_and_bad_block_are_rejected(lib):
     assert prefill(lib, m, s) == -1
 
 
+def test_staleness_validation(lib):
+    m, s = model_desc(), seq_desc()
+    cb, wb = sizes(lib, m, s)
+    s.kv_cache_bytes, s.workspace_bytes = cb, wb
+    f = lib.cdll.dllm_cache_staleness
+    for blk in (-1, 4):
+        assert f(C.byref(m), C.byref(s), blk, FAKE, cb, FAKE, None) == -6
+    assert f(C.byref(m), C.byref(s), 0, None, cb, FAKE, None) == -1
+    assert f(C.byref(m), C.byref(s), 0, FAKE, cb, None, None) == -1
+    assert f(C.byref(m), C.byref(s), 0, FAKE, cb - 1, FAKE, None) == -4
+    s.cache_mode = bd.CACHE_NONE
+    assert f(C.byref(m), C.byref(s), 0, FAKE, cb, FAKE, None) == -6
+
+
 def test_null_descriptors(lib):
     assert lib.cdll.dllm_prefill_cache(None, None, None) == -1
     assert lib.cdll.dllm_workspace_bytes(None, None) == 0

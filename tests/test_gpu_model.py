@@ -329,3 +329,62 @@ def test_first_step_full_size_matches_oracle_sample(lib, name):
         assert abs(conf[r] - row["conf"]) <= row["conf"] * np.expm1(2 * dl) + 1e-6, f"row {r}"
     del model
     torch.cuda.empty_cache()
+
+
+def staleness_tol(c, r):
+    """Bound on how far a cosine moves when each of its two vectors carries a relative
+    L2 error of at most r: to first order |dc| <= 2 r sqrt(1 - c^2) <= 2 r sqrt(2 (1 - c))
+    (the gradient of the cosine in a is orthogonal to a, of length sqrt(1 - c^2) / |a|),
+    plus r^2 for the second order.  The bound is concave in the cosine, so it also bounds
+    the mean, by Jensen, and the minimum (c - bound(c) increases with c)."""
+    return 2.0 * r * np.sqrt(2.0 * np.maximum(1.0 - c, 0.0)) + r * r + 1e-6
+
+
+@pytest.mark.parametrize("kind,mode", [("f32", "dual"), ("f32", "prefix"), ("bf16", "dual"),
+                                       ("bf16", "prefix")])
+def test_cache_staleness_matches_oracle(lib, kind, mode):
+    """dllm_cache_staleness against the oracle's measure on the same token state: 1 right
+    after a refresh, layer 0 still 1 after block-only changes, and per layer the mean and
+    minimum cosine of cached and exact K/V within the bound implied by the K/V error of
+    the two sides (fp32: 1e-5 relative; bf16: 1e-2, a few bf16 ulps)."""
+    if kind == "f32":
+        wl = replace(synth.WORKLOADS["tiny_dual"], cache_mode=mode)
+        r = 1e-5
+    else:
+        wl = small_bf16(Hq=2, Hkv=1, mode=mode, B=2, K=32, P=40)
+        r = 1e-2
+    M = om.OracleModel(wl)
+    prompt = synth.make_prompt(wl)
+    osess = OSession(M, prompt, wl.gen_len, wl.block_len, wl.threshold, mode)
+    gsess = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, wl.threshold, mode)
+    worst = 0.0
+    for b in range(min(osess.n_blocks, 2)):
+        osess.refresh()
+        gsess.tokens.copy_(torch.from_numpy(osess.tokens.astype(np.int32)))
+        if b == 0:
+            gsess.prefill()
+        else:
+            gsess.refresh(b)
+        g = gsess.staleness(b)
+        for key in ("k_mean", "k_min", "v_mean", "v_min"):
+            np.testing.assert_allclose(g[key], 1.0, atol=1e-6)
+        for _ in range(2):
+            if osess.block_done(b):
+                break
+            osess.step(b)
+            gsess.tokens.copy_(torch.from_numpy(osess.tokens.astype(np.int32)))
+            ost, oratio = osess.staleness(b)
+            g = gsess.staleness(b)
+            assert g["reuse"] == pytest.approx(oratio, abs=1e-12)
+            for j, kv in enumerate("kv"):
+                np.testing.assert_allclose(g[kv + "_mean"][0], 1.0, atol=1e-6)
+                np.testing.assert_allclose(g[kv + "_min"][0], 1.0, atol=1e-6)
+                for i, stat in enumerate(("_mean", "_min")):
+                    got = g[kv + stat].astype(np.float64)
+                    ref = ost[:, j, i]
+                    err = np.abs(got - ref)
+                    worst = max(worst, float(err.max()))
+                    assert np.all(err <= staleness_tol(ref, r)), (b, kv + stat, got, ref)
+        while not osess.block_done(b):
+            osess.step(b)
+    print(f"worst staleness difference {worst:.2e}")
