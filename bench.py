@@ -409,7 +409,8 @@ def main():
     lib.call("dllm_profile_select", -1)
     for i, st in enumerate(stats):
         log(f"step {i}: {st['ms_total']:.1f} ms ({st['steps']} cached steps, {st['refreshes']} "
-            f"refreshes; refresh {st['ms_refresh']:.1f} ms, steps {st['ms_step']:.1f} ms)")
+            f"refreshes, {st['speculative_steps']} speculative; refresh {st['ms_refresh']:.1f} ms, "
+            f"steps {st['ms_step']:.1f} ms)")
 
     toks = wl.batch * wl.gen_len * a.steps
     value = toks / dt

@@ -49,7 +49,8 @@ class SeqDesc(C.Structure):
 class Stats(C.Structure):
     _fields_ = [("steps", C.c_int32), ("refreshes", C.c_int32), ("tokens", C.c_int32),
                 ("blocks", C.c_int32), ("ms_total", C.c_double), ("ms_refresh", C.c_double),
-                ("ms_step", C.c_double), ("steps_per_block", C.POINTER(C.c_int32))]
+                ("ms_step", C.c_double), ("steps_per_block", C.POINTER(C.c_int32)),
+                ("speculative_steps", C.c_int32)]
 
 
 class DllmError(RuntimeError):

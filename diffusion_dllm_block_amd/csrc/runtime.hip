@@ -1,5 +1,6 @@
 // libdllm host runtime: argument validation, workspace planning, the launch sequences of
 // prefill / refresh / block step, the generation loop and the C ABI (include/dllm.h).
+#include <algorithm>
 #include <chrono>
 #include <cmath>
 #include <cstdarg>
@@ -598,42 +599,72 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
   if (st) return st;
   hipStream_t hs = (hipStream_t)stream;
   Ctx c{d, m, s, w, (char*)s->workspace, hs};
-  int32_t* host = nullptr;  // pinned: [B] remaining
-  HIP_TRY(hipHostMalloc((void**)&host, sizeof(int32_t) * d.B, hipHostMallocDefault));
+  // Each step's verdict (mask tokens left per sequence) goes to one of two pinned host
+  // slots, with an event behind the copy.  The host keeps the next step queued while it
+  // waits for the previous verdict, so the device never waits for the host to launch a
+  // step.  Every step decodes at least one token of each unfinished sequence, so a step
+  // that follows a verdict of at most one token left per sequence finishes the block:
+  // no further step is queued then.  With two or more left, the step after the one in
+  // flight is queued on speculation; if the one in flight finishes the block, the
+  // speculative step finds nothing masked and changes no token (its K/V writes are
+  // overwritten by the next refresh), costing one step of device time.
+  int32_t* host = nullptr;  // pinned: [2][B] remaining
+  HIP_TRY(hipHostMalloc((void**)&host, sizeof(int32_t) * 2 * d.B, hipHostMallocDefault));
   struct Free { int32_t* p; ~Free() { if (p) (void)hipHostFree(p); } } guard{host};
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  struct Ev { hipEvent_t* e; ~Ev() { for (int i = 0; i < 2; ++i) if (e[i]) (void)hipEventDestroy(e[i]); } } eguard{ev};
+  for (int i = 0; i < 2; ++i) HIP_TRY(hipEventCreateWithFlags(&ev[i], hipEventDisableTiming));
   const double t_start = now_ms();
   double ms_ref = 0, ms_step = 0;
-  int steps = 0, refreshes = 0;
+  int steps = 0, refreshes = 0, wasted = 0;
   for (int b = 0; b < d.nblocks; ++b) {
-    // refresh (prefill for block 0) fused with the block's first step
+    int issued = 0;  // steps of this block enqueued (the first fused with the refresh)
+    auto issue = [&]() -> dllm_status {
+      const bool full = issued == 0 || d.mode == DLLM_CACHE_NONE;
+      dllm_status r = full ? do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr)
+                           : do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+      if (r) return r;
+      const int slot = issued & 1;
+      HIP_TRY(hipMemcpyAsync(host + slot * d.B, c.at<int>(w.rem), d.B * sizeof(int32_t),
+                             hipMemcpyDeviceToHost, hs));
+      HIP_TRY(hipEventRecord(ev[slot], hs));
+      ++issued;
+      return DLLM_OK;
+    };
     double t0 = now_ms();
-    st = do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+    st = issue();
     if (st) return st;
-    ++refreshes;
-    HIP_TRY(hipMemcpyAsync(host, c.at<int>(w.rem), d.B * sizeof(int32_t), hipMemcpyDeviceToHost, hs));
-    HIP_TRY(hipStreamSynchronize(hs));
-    ms_ref += now_ms() - t0;
-    bool any = false;
-    for (int i = 0; i < d.B; ++i) any |= host[i] != 0;
-    int n = 1;
-    t0 = now_ms();
-    while (any) {
-      st = (d.mode == DLLM_CACHE_NONE)
-               ? do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr)
-               : do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
-      if (st) return st;
-      HIP_TRY(hipMemcpyAsync(host, c.at<int>(w.rem), d.B * sizeof(int32_t), hipMemcpyDeviceToHost, hs));
-      HIP_TRY(hipStreamSynchronize(hs));
-      ++n;
-      any = false;
-      for (int i = 0; i < d.B; ++i) any |= host[i] != 0;
-      if (n > d.K) return fail(DLLM_E_STATE, "block %d did not finish in %d steps", b, d.K);
+    int confirmed = 0;  // steps whose verdict has been read
+    for (;;) {
+      const int slot = confirmed & 1;
+      HIP_TRY(hipEventSynchronize(ev[slot]));
+      ++confirmed;
+      int left = 0;
+      for (int i = 0; i < d.B; ++i) left = std::max(left, (int)host[slot * d.B + i]);
+      if (confirmed == 1) {
+        ms_ref += now_ms() - t0;
+        t0 = now_ms();
+      }
+      if (left == 0) break;
+      if (confirmed >= d.K) return fail(DLLM_E_STATE, "block %d did not finish in %d steps", b, d.K);
+      if (issued == confirmed) {  // the next step is needed
+        st = issue();
+        if (st) return st;
+      }
+      if (left >= 2 && issued == confirmed + 1 && issued < d.K) {  // the one after, maybe
+        st = issue();
+        if (st) return st;
+      }
     }
     ms_step += now_ms() - t0;
+    const int n = confirmed;
+    wasted += issued - confirmed;
     steps += n;
+    ++refreshes;
     if (d.mode == DLLM_CACHE_NONE) refreshes += n - 1;  // every step was a full forward
     if (out && out->steps_per_block) out->steps_per_block[b] = n;
   }
+  HIP_TRY(hipStreamSynchronize(hs));  // a speculative step may still be running
   if (out) {
     out->steps = steps;
     out->refreshes = refreshes;
@@ -642,6 +673,7 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
     out->ms_total = now_ms() - t_start;
     out->ms_refresh = ms_ref;
     out->ms_step = ms_step;
+    out->speculative_steps = wasted;
   }
   return DLLM_OK;
 }

@@ -178,7 +178,8 @@ class Session:
         self.lib.call("dllm_generate", *self._args(), bd.stream_handle(stream), C.byref(st))
         stats = {"steps": st.steps, "refreshes": st.refreshes, "tokens": st.tokens,
                  "blocks": st.blocks, "ms_total": st.ms_total, "ms_refresh": st.ms_refresh,
-                 "ms_step": st.ms_step, "steps_per_block": list(spb)[: self.n_blocks]}
+                 "ms_step": st.ms_step, "steps_per_block": list(spb)[: self.n_blocks],
+                 "speculative_steps": st.speculative_steps}
         return self.tokens[:, self.P:].cpu().numpy(), stats
 
     def reset_tokens(self, prompt=None):

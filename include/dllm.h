@@ -131,8 +131,11 @@ typedef struct {
   int32_t refreshes;                  /* full forwards run (prefill included)            */
   int32_t tokens;                     /* tokens generated (batch * gen_len)              */
   int32_t blocks;
-  double ms_total, ms_refresh, ms_step; /* host wall clock, stream-synchronised          */
+  double ms_total, ms_refresh, ms_step; /* host wall clock: whole call; from each block's
+                                         refresh to its verdict; the block's later steps */
   int32_t* steps_per_block;           /* optional host array [gen_len/block_len], or NULL */
+  int32_t speculative_steps;          /* steps queued ahead that found the block already
+                                         finished (decode nothing; not in `steps`)       */
 } dllm_stats;
 
 /* Sizes (host only, no device work).  Return 0 if the descriptors are invalid.       */
@@ -181,7 +184,11 @@ dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, 
 
 /* Whole generation: for every block, dllm_refresh_step (the prefill for block 0), then
  * cached steps until the block has no mask token left (one 4*batch-byte device-to-host
- * read per step); with DLLM_CACHE_NONE every step is a dllm_refresh_step.
+ * read per step); with DLLM_CACHE_NONE every step is a dllm_refresh_step.  The next
+ * step is queued before the previous step's read completes whenever that read may not
+ * end the block (some sequence had two or more masks left), so the device does not wait
+ * for launches; such a step that finds the block finished decodes nothing and is
+ * counted in speculative_steps.  Tokens are those of the step-by-step loop.
  * Synchronous.  `out` may be NULL.                                                   */
 dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s,
                           dllm_stream_t stream, dllm_stats* out);

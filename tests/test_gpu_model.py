@@ -290,6 +290,39 @@ def test_generate_properties_llada_shape_two_blocks(lib):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("mode,tau", [("dual", 0.9), ("dual", 0.3), ("prefix", 0.5),
+                                      ("none", 0.6)])
+def test_generate_matches_the_step_by_step_loop(lib, mode, tau):
+    """dllm_generate queues the next step before reading the previous step's verdict
+    (and on speculation, one more when that verdict left two or more masks): tokens and
+    steps per block must equal a host loop that reads every verdict before the next
+    step.  Low thresholds decode several tokens per step, so speculative steps that
+    find their block finished occur and must change nothing."""
+    wl = small_bf16(Hq=2, Hkv=1, mode="dual" if mode == "none" else mode, B=2, K=16, P=40)
+    model = gpu_model(lib, wl)
+    prompt = synth.make_prompt(wl)
+    s = Session(model, prompt, wl.gen_len, wl.block_len, tau, mode)
+    spb = []
+    for b in range(s.n_blocks):
+        s.refresh_step(b, logits=False)
+        n = 1
+        while int(s.remaining.max().item()) > 0:
+            if mode == "none":
+                s.refresh_step(b, logits=False)
+            else:
+                s.step(b, logits=False)
+            n += 1
+            assert n <= wl.block_len
+        spb.append(n)
+    want = s.tokens.cpu().numpy()[:, s.P:].copy()
+    g = Session(model, prompt, wl.gen_len, wl.block_len, tau, mode)
+    got, st = g.generate()
+    assert np.array_equal(got, want)
+    assert st["steps_per_block"] == spb and st["steps"] == sum(spb)
+    assert 0 <= st["speculative_steps"] <= s.n_blocks
+    print(f"steps per block {spb}, speculative steps {st['speculative_steps']}")
+
+
 FULL_SIZE = ["llada8b_dual_p1000_g1024", "llada8b_prefix_p256_g256", "dream7b_dual_b8_p512_g512"]
 
 
