@@ -233,6 +233,9 @@ GEMM_CASES = [
     ("skinny_m7_ragged_n", 7, 1000, 512, "bf16"),
     ("skinny_m50_two_tiles", 50, 384, 1024, "bf16"),
     ("skinny_m32_down_k12288", 32, 512, 12288, "bf16"),
+    # the 8B down projection (6 K ranges of 2048 over 42-43 workgroups each), 16 rows too
+    ("skinny_m32_down_full", 32, 4096, 12288, "bf16"),
+    ("skinny_m16_down_full", 16, 4096, 12288, "bf16"),
     ("tiled_m300_ragged", 300, 384, 512, "bf16"),
     # mid (64 < M <= 256): every tile split over K / whole tiles plus a split ragged
     # last round (2 rounds of 256 whole tiles, 9 tail tiles in 4 K pieces) / ragged N
