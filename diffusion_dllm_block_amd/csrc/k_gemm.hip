@@ -188,13 +188,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int kw0 = split * C::KW;      // the workgroup's K range
   const int ks0 = kw0 + w * KS;       // this wave's K sub-range
 
-  {  // activation slice -> LDS (rows >= M read row M-1; their outputs are never used)
+  auto wptr = [&](int grp) {  // columns past Nv read a clamped valid row (never used)
+    const int vc = min(grp * 16 + ln, Nv - 1);
+    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + ks0 + 8 * g;
+  };
+  u32x4 wr[C::NLOAD];
+  {
+    // activation slice -> LDS (rows >= M read row M-1; their outputs are never used).
+    // The first group's weight loads are issued between the activation loads and their
+    // LDS stores: the stores then wait only for the activation loads (issued first), and
+    // the weight stream's first HBM round trip overlaps the staging instead of following
+    // it.  The weight loads go in t order, like the refills in the loop, so that the
+    // loop's wait counts are the same on entry and on the back edge.
     u32x4 xr[C::XV];
 #pragma unroll
     for (int i = 0; i < C::XV; ++i) {
       const int ee = tid + 512 * i;
       const int r = ee / (C::KW / 8), c8 = ee % (C::KW / 8);
       xr[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(r, M - 1) * ldx + kw0 + 8 * c8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* wp = wptr(min(wid, ngrp - 1));
+#pragma unroll
+    for (int t = 0; t < C::NLOAD; ++t) {
+      wr[t] = *reinterpret_cast<const u32x4*>(wp + 32 * t);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < C::XV; ++i) {
@@ -204,26 +222,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
   __syncthreads();
-  if (wid >= ngrp) return;  // uniform over the workgroup; no barrier follows for it
 
-  auto wptr = [&](int grp) {  // columns past Nv read a clamped valid row (never used)
-    const int vc = min(grp * 16 + ln, Nv - 1);
-    return W + (int64_t)wrow_s2<MAP>(vc, F) * K + ks0 + 8 * g;
-  };
-  u32x4 wr[C::NLOAD];
-  {
-    // issued in t order, like the refills in the loop, so that the loop's wait counts
-    // are the same on entry and on the back edge
-    const uint16_t* wp = wptr(wid);
-#pragma unroll
-    for (int t = 0; t < C::NLOAD; ++t) {
-      wr[t] = *reinterpret_cast<const u32x4*>(wp + 32 * t);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
+  // A do-while with no exit between the loads above and the loop: an exit branch here
+  // lets the compiler sink the first weight loads below the barrier.  The host launches
+  // at most ngrp workgroups per K range, so wid < ngrp; the partial store is guarded
+  // anyway (uniform over the workgroup).
   const uint16_t* xs = &Xs[ln * C::LDX + w * KS + 8 * g];
-  for (int grp = wid; grp < ngrp; grp += nw) {
+  int grp = wid;
+  do {
     const bool has_next = grp + nw < ngrp;
     // refill source: the next group, or (after the last group) this wave's first weight
     // line, which stays cached; the same offsets keep the loads' addresses immediate
@@ -248,15 +254,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[w][mt * 4 + r][l] = acc[mt][r];
     __syncthreads();
-    float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
-    for (int sl = w; sl < C::SLOTS; sl += 8) {
-      float v = red[0][sl][l];
+    if (grp < ngrp) {
+      float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
+      for (int sl = w; sl < C::SLOTS; sl += 8) {
+        float v = red[0][sl][l];
 #pragma unroll
-      for (int ww = 1; ww < 8; ++ww) v += red[ww][sl][l];
-      blk[sl * 64 + l] = v;
+        for (int ww = 1; ww < 8; ++ww) v += red[ww][sl][l];
+        blk[sl * 64 + l] = v;
+      }
     }
     __syncthreads();  // red is rewritten by the next group
-  }
+    grp += nw;
+  } while (grp < ngrp);
 }
 
 // ============================================================================
