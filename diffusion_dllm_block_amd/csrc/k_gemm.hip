@@ -891,10 +891,26 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     const float4 a = scale4(sum_split4(pv, m, c), r);
     const float4 b = scale4(sum_split4(pv, m, cb), r);
     const int hs = pv.vbase / 128 + hl;
-    qkv_pair(e, m, hs, d + 0, a.x, b.x);
-    qkv_pair(e, m, hs, d + 1, a.y, b.y);
-    qkv_pair(e, m, hs, d + 2, a.z, b.z);
-    qkv_pair(e, m, hs, d + 3, a.w, b.w);
+    if (hs < e.Hq + e.Hkv) {
+      // q or k: the four rotated pairs as two 8-byte stores (dims d..d+3, d+64..d+67)
+      const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
+      uint16_t* dst = (hs < e.Hq)
+          ? (uint16_t*)e.qo + (((int64_t)bs * e.Hq + hs) * e.R + ri) * 128
+          : (uint16_t*)e.kc + (((int64_t)bs * e.Hkv + (hs - e.Hq)) * e.Sp + pos) * 128;
+      const float4 cs = *reinterpret_cast<const float4*>(e.rcos + (int64_t)pos * 64 + d);
+      const float4 sn = *reinterpret_cast<const float4*>(e.rsin + (int64_t)pos * 64 + d);
+      *reinterpret_cast<u16x4*>(dst + d) =
+          u16x4{f2bf(a.x * cs.x - b.x * sn.x), f2bf(a.y * cs.y - b.y * sn.y),
+                f2bf(a.z * cs.z - b.z * sn.z), f2bf(a.w * cs.w - b.w * sn.w)};
+      *reinterpret_cast<u16x4*>(dst + d + 64) =
+          u16x4{f2bf(b.x * cs.x + a.x * sn.x), f2bf(b.y * cs.y + a.y * sn.y),
+                f2bf(b.z * cs.z + a.z * sn.z), f2bf(b.w * cs.w + a.w * sn.w)};
+    } else {
+      qkv_pair(e, m, hs, d + 0, a.x, b.x);
+      qkv_pair(e, m, hs, d + 1, a.y, b.y);
+      qkv_pair(e, m, hs, d + 2, a.z, b.z);
+      qkv_pair(e, m, hs, d + 3, a.w, b.w);
+    }
   }
 }
 
