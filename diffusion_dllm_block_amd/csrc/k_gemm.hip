@@ -846,8 +846,14 @@ __device__ __forceinline__ void qkv_pair(const EpiArgs& e, int m, int hs, int d,
 // (pv.order): the 64-column order of wrow_s2 (SwiGLU: 32 gate columns then the matching
 // 32 up columns; QKV: one head slot per 128 columns, dims 0..31, 64..95, 32..63,
 // 96..127) or the large tiles' 128-column order of wrow_of (64 + 64; dims in order).
+// QKV: workgroups [0, qk_blocks) take the q and k head slots (the first nqk slots of
+// the span), one thread per (row, slot, 4 rotated pairs); the rest take 32 rows x 32
+// dims of one V head slot each, transposed through LDS so that the stores into the
+// blocked Vt cache (keys contiguous) are 32 consecutive keys per dim instead of one
+// 2-byte store per key.
 template <int EPI>
-__global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
+__global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e, int nqk,
+                                                       int qk_blocks) {
   const int M = pv.M, Nt = pv.N;
   const int64_t i4 = (blockIdx.x * (int64_t)blockDim.x + threadIdx.x) * 4;
   if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
@@ -877,8 +883,36 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
     y[0] = swiglu_bf16(gt.x, up.x); y[1] = swiglu_bf16(gt.y, up.y);
     y[2] = swiglu_bf16(gt.z, up.z); y[3] = swiglu_bf16(gt.w, up.w);
   } else if constexpr (EPI == EPI_QKV) {
+    if ((int)blockIdx.x >= qk_blocks) {  // V: uniform per workgroup
+      __shared__ float tile[32][33];     // [row][dim]; odd stride: conflict-free columns
+      const int nv = Nt / 128 - nqk;
+      const int vb = (int)blockIdx.x - qk_blocks;
+      const int hl = nqk + (vb >> 2) % nv, m0 = ((vb >> 2) / nv) * 32, q = vb & 3;
+      // virtual columns [32q, 32q + 32) of the slot hold one run of 32 dims: the 64-column
+      // order keeps dims 0-31, 64-95, 32-63, 96-127; the 128-column order keeps them in place
+      const int dbase = pv.order ? 32 * q : (q & 1) * 64 + (q >> 1) * 32;
+      const int t = threadIdx.x;
+      {
+        const int mr = t >> 3, m = m0 + mr, j = 4 * (t & 7);
+        if (m < M) {
+          const float4 v = scale4(sum_split4(pv, m, 128 * hl + 32 * q + j), row_rms_factor(e, m));
+          tile[mr][j] = v.x; tile[mr][j + 1] = v.y; tile[mr][j + 2] = v.z; tile[mr][j + 3] = v.w;
+        }
+      }
+      __syncthreads();
+      const int mr = t & 31, m = m0 + mr, d0 = (t >> 5) * 4;
+      if (m < M) {
+        const int bs = m / e.R, ri = m % e.R, pos = e.pos0 + ri;
+        const int hs = pv.vbase / 128 + hl;
+        uint16_t* dst = (uint16_t*)e.vtc +
+                        ((int64_t)bs * e.Hkv + (hs - e.Hq - e.Hkv)) * 128 * (int64_t)e.Sp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[vt_off(dbase + d0 + i, pos, 128)] = f2bf(tile[mr][d0 + i]);
+      }
+      return;
+    }
     // (row m, head slot hs, dims d..d+3 < 64) -> pairs (d, d+64); head_dim 128
-    const int nslot = Nt / 128;
+    const int nslot = nqk;
     if (i4 >= (int64_t)M * nslot * 64) return;
     const int m = (int)(i4 / (nslot * 64));
     const int rem = (int)(i4 % (nslot * 64));
@@ -916,17 +950,25 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e) {
 
 hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e, hipStream_t st) {
   int64_t n4 = 0;
+  int nqk = 0, qkb = 0, vblocks = 0;
   if (epi == EPI_STORE || epi == EPI_F32) n4 = (int64_t)pv.M * pv.N / 4;
   else if (epi == EPI_SWIGLU) n4 = (int64_t)pv.M * (pv.N / 2) / 4;
-  else if (epi == EPI_QKV) n4 = (int64_t)pv.M * (pv.N / 128) * 16;
-  else return hipErrorInvalidValue;
-  if (n4 <= 0) return hipSuccess;
-  const unsigned blocks = (unsigned)((n4 + 255) / 256);
+  else if (epi == EPI_QKV) {
+    // the span's slots are q and k heads up to slot Hq + Hkv, V heads after it
+    const int nslot = pv.N / 128;
+    nqk = std::max(0, std::min(nslot, e.Hq + e.Hkv - pv.vbase / 128));
+    n4 = (int64_t)pv.M * nqk * 16;
+    qkb = (int)((n4 + 255) / 256);
+    vblocks = (nslot - nqk) * ((pv.M + 31) / 32) * 4;
+  } else return hipErrorInvalidValue;
+  const int64_t blocks64 = (n4 + 255) / 256 + vblocks;
+  if (blocks64 <= 0) return hipSuccess;
+  const unsigned blocks = (unsigned)blocks64;
   switch (epi) {
-    case EPI_STORE: reduce_epilogue<EPI_STORE><<<blocks, 256, 0, st>>>(pv, e); break;
-    case EPI_F32: reduce_epilogue<EPI_F32><<<blocks, 256, 0, st>>>(pv, e); break;
-    case EPI_SWIGLU: reduce_epilogue<EPI_SWIGLU><<<blocks, 256, 0, st>>>(pv, e); break;
-    case EPI_QKV: reduce_epilogue<EPI_QKV><<<blocks, 256, 0, st>>>(pv, e); break;
+    case EPI_STORE: reduce_epilogue<EPI_STORE><<<blocks, 256, 0, st>>>(pv, e, 0, 0); break;
+    case EPI_F32: reduce_epilogue<EPI_F32><<<blocks, 256, 0, st>>>(pv, e, 0, 0); break;
+    case EPI_SWIGLU: reduce_epilogue<EPI_SWIGLU><<<blocks, 256, 0, st>>>(pv, e, 0, 0); break;
+    case EPI_QKV: reduce_epilogue<EPI_QKV><<<blocks, 256, 0, st>>>(pv, e, nqk, qkb); break;
   }
   return hipGetLastError();
 }
