@@ -599,11 +599,11 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
   if (st) return st;
   hipStream_t hs = (hipStream_t)stream;
   Ctx c{d, m, s, w, (char*)s->workspace, hs};
-  // Each step's verdict (mask tokens left per sequence) goes to one of two pinned host
+  // Each step's outcome (mask tokens left per sequence) goes to one of two pinned host
   // slots, with an event behind the copy.  The host keeps the next step queued while it
-  // waits for the previous verdict, so the device never waits for the host to launch a
+  // waits for the previous outcome, so the device never waits for the host to launch a
   // step.  Every step decodes at least one token of each unfinished sequence, so a step
-  // that follows a verdict of at most one token left per sequence finishes the block:
+  // that follows an outcome of at most one token left per sequence finishes the block:
   // no further step is queued then.  With two or more left, the step after the one in
   // flight is queued on speculation; if the one in flight finishes the block, the
   // speculative step finds nothing masked and changes no token (its K/V writes are
@@ -634,7 +634,7 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
     double t0 = now_ms();
     st = issue();
     if (st) return st;
-    int confirmed = 0;  // steps whose verdict has been read
+    int confirmed = 0;  // steps whose outcome has been read
     for (;;) {
       const int slot = confirmed & 1;
       HIP_TRY(hipEventSynchronize(ev[slot]));

@@ -132,7 +132,7 @@ typedef struct {
   int32_t tokens;                     /* tokens generated (batch * gen_len)              */
   int32_t blocks;
   double ms_total, ms_refresh, ms_step; /* host wall clock: whole call; from each block's
-                                         refresh to its verdict; the block's later steps */
+                                         refresh to its outcome; the block's later steps */
   int32_t* steps_per_block;           /* optional host array [gen_len/block_len], or NULL */
   int32_t speculative_steps;          /* steps queued ahead that found the block already
                                          finished (decode nothing; not in `steps`)       */

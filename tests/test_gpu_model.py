@@ -293,9 +293,9 @@ def test_generate_properties_llada_shape_two_blocks(lib):
 @pytest.mark.parametrize("mode,tau", [("dual", 0.9), ("dual", 0.3), ("prefix", 0.5),
                                       ("none", 0.6)])
 def test_generate_matches_the_step_by_step_loop(lib, mode, tau):
-    """dllm_generate queues the next step before reading the previous step's verdict
-    (and on speculation, one more when that verdict left two or more masks): tokens and
-    steps per block must equal a host loop that reads every verdict before the next
+    """dllm_generate queues the next step before reading the previous step's outcome
+    (and on speculation, one more when that outcome left two or more masks): tokens and
+    steps per block must equal a host loop that reads every outcome before the next
     step.  Low thresholds decode several tokens per step, so speculative steps that
     find their block finished occur and must change nothing."""
     wl = small_bf16(Hq=2, Hkv=1, mode="dual" if mode == "none" else mode, B=2, K=16, P=40)
