@@ -321,6 +321,32 @@ def ablation(model, wl, torch):
     return {"workload": wl.name, "runs": out}
 
 
+def staleness_trace(sess, wl, blocks: int):
+    """Cache staleness across the steps of the first `blocks` blocks (dllm_cache_staleness
+    before every cached step): per step, the cosine similarity of the cached and the
+    exact K and V at the positions the step reads from the cache, averaged over layers,
+    its worst layer mean and worst single vector, and the reuse ratio.  Random-init
+    weights: a check that the instrumentation runs at the real shape, not a measurement of
+    the pages' trained-model claim."""
+    out = []
+    sess.reset_tokens()
+    for b in range(min(blocks, sess.n_blocks)):
+        o = sess.refresh_step(b, logits=False)
+        n = 1
+        while int(o["remaining"].max().item()) > 0:
+            st = sess.staleness(b)
+            out.append({"block": b, "step": n,
+                        "k_mean": round(float(st["k_mean"].mean()), 6),
+                        "v_mean": round(float(st["v_mean"].mean()), 6),
+                        "worst_layer_mean": round(float(min(st["k_mean"].min(),
+                                                            st["v_mean"].min())), 6),
+                        "worst_vector": round(float(min(st["k_min"].min(), st["v_min"].min())), 6),
+                        "reuse": round(st["reuse"], 4)})
+            o = sess.step(b, logits=False)
+            n += 1
+    return {"workload": wl.name, "steps": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +358,9 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the kernel-only rates")
     ap.add_argument("--ablation", action="store_true",
                     help="cache on/off x parallel decoding on/off on the workload, one JSON line")
+    ap.add_argument("--staleness", type=int, default=0, metavar="BLOCKS",
+                    help="cache staleness before every cached step of the first BLOCKS "
+                         "blocks, one JSON line (no timing)")
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the kernel-only rates (no generation; for profiling)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -382,6 +411,9 @@ def main():
     if a.ablation:
         del sess
         print(json.dumps({"ablation": ablation(model, wl, torch)}), flush=True)
+        return
+    if a.staleness:
+        print(json.dumps({"staleness": staleness_trace(sess, wl, a.staleness)}), flush=True)
         return
 
     for i in range(a.warmup):
