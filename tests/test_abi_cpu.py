@@ -161,3 +161,10 @@ def test_kernel_entry_validation(lib):
     assert lib.cdll.dllm_profile_select_every(99, 1) == -7
     assert lib.cdll.dllm_profile_select_every(0, 0) == -7
     assert lib.cdll.dllm_profile_select_every(-1, 7) == 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No fallback: without the built HIP library the binding raises instead of running
+    anything else."""
+    with pytest.raises(FileNotFoundError):
+        bd.Lib(str(tmp_path / "libdllm.so"))
