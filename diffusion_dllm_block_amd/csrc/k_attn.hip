@@ -211,13 +211,19 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
     // The next sub-tile is always requested, past the end too (clamped addresses, never
     // consumed): with no load under a branch, the wait before each consume counts only
     // the sub-tile it needs, and the following one stays in flight.
+    // A do-while: a loop that may run zero times lets the compiler sink the first
+    // sub-tile's loads (issued above, before the Q tile's LDS store) below the barrier,
+    // behind a test on nsub.  The plan gives every wave nsub >= 1; a first sub-tile with
+    // no key below S would be all masked and leave the state unchanged.
     KVTile16 tb;
-    for (int n = 0; n < nsub; n += 2) {
+    int n = 0;
+    do {
       load_kv16(tb, kbase, vbase, wkey0 + 32 * (n + 1), li, j, S, Sp);
       consume(ta, wkey0 + 32 * n);
       load_kv16(ta, kbase, vbase, wkey0 + 32 * (n + 2), li, j, S, Sp);
       if (n + 1 < nsub) consume(tb, wkey0 + 32 * (n + 1));
-    }
+      n += 2;
+    } while (n < nsub);
   }
 
   // ---- merge the 4 waves (fixed order)
