@@ -183,6 +183,10 @@ ATTN_CASES = [
     ("llada_block32_kv2024", 1, 32, 32, 32, 2024, "bf16"),
     ("gqa_7to1_b2", 2, 28, 4, 32, 1000, "bf16"),
     ("gqa_7to1_b8_multi_subtile", 8, 28, 4, 32, 1024, "bf16"),
+    # several sub-tiles per wave with an odd count (3 and 5) and a ragged last chunk
+    # (chunks of 384 and 640 keys)
+    ("multi_subtile_odd_ragged", 2, 32, 32, 32, 1500, "bf16"),
+    ("multi_subtile_long_ragged", 1, 32, 32, 32, 4100, "bf16"),
     ("ragged_rows_keys", 1, 4, 2, 20, 77, "bf16"),
     ("two_row_tiles", 1, 2, 1, 64, 300, "bf16"),
     ("flash_many_rows", 1, 2, 2, 200, 333, "bf16"),
