@@ -361,6 +361,9 @@ def main():
     ap.add_argument("--staleness", type=int, default=0, metavar="BLOCKS",
                     help="cache staleness before every cached step of the first BLOCKS "
                          "blocks, one JSON line (no timing)")
+    ap.add_argument("--graphs", action="store_true",
+                    help="time generations with each block's cached steps replayed from a "
+                         "HIP graph (no kernel-class timing), one JSON line")
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the kernel-only rates (no generation; for profiling)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -414,6 +417,25 @@ def main():
         return
     if a.staleness:
         print(json.dumps({"staleness": staleness_trace(sess, wl, a.staleness)}), flush=True)
+        return
+    if a.graphs:
+        res = {}
+        for graphs in (False, True, False, True):
+            for _ in range(a.warmup):
+                sess.reset_tokens()
+                sess.generate(graphs=graphs)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(a.steps):
+                sess.reset_tokens()
+                _, st = sess.generate(graphs=graphs)
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - t0) / a.steps
+            key = "graphs" if graphs else "eager"
+            res.setdefault(key, []).append(round(wl.batch * wl.gen_len / dt, 2))
+            log(f"{key}: {dt * 1e3:.1f} ms per generation ({st['steps']} steps)")
+        print(json.dumps({"graph_replay": {"workload": wl.name, "tokens_per_s": res}}),
+              flush=True)
         return
 
     for i in range(a.warmup):

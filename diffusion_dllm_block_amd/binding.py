@@ -72,6 +72,7 @@ _SIGS = {
     "dllm_refresh_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P,
                                _P]),
     "dllm_generate": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _P, C.POINTER(Stats)]),
+    "dllm_generate_graphs": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _P, C.POINTER(Stats)]),
     "dllm_kernel_workspace_bytes": (C.c_size_t, [_I] * 7),
     "dllm_kernel_block_attention": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
                                          C.c_size_t, _P]),

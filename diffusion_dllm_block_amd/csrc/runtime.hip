@@ -591,13 +591,27 @@ dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, 
   return do_refresh_step(c, block, d_n_unmasked, d_remaining, d_logits, d_conf, d_argmax);
 }
 
-dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm_stream_t stream,
-                          dllm_stats* out) {
+static dllm_status generate_impl(const dllm_model_desc* m, const dllm_seq_desc* s,
+                                 dllm_stream_t stream, bool graphs, dllm_stats* out) {
   Dims d;
   Ws w;
   dllm_status st = setup(m, s, &d, &w);
   if (st) return st;
+  if (graphs && g_prof.cls != DLLM_K_NONE)
+    return fail(DLLM_E_UNSUPPORTED, "kernel-class timing is not available with graph replay");
   hipStream_t hs = (hipStream_t)stream;
+  // The legacy null stream cannot be captured: graph replay then runs on a stream of its
+  // own, after the null stream's pending work (the call is synchronous either way).
+  hipStream_t own = nullptr;
+  struct OwnStream {
+    hipStream_t* s;
+    ~OwnStream() { if (*s) { (void)hipStreamSynchronize(*s); (void)hipStreamDestroy(*s); } }
+  } oguard{&own};
+  if (graphs && hs == nullptr) {
+    HIP_TRY(hipStreamSynchronize(nullptr));
+    HIP_TRY(hipStreamCreateWithFlags(&own, hipStreamNonBlocking));
+    hs = own;
+  }
   Ctx c{d, m, s, w, (char*)s->workspace, hs};
   // Each step's outcome (mask tokens left per sequence) goes to one of two pinned host
   // slots, with an event behind the copy.  The host keeps the next step queued while it
@@ -614,15 +628,48 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
   hipEvent_t ev[2] = {nullptr, nullptr};
   struct Ev { hipEvent_t* e; ~Ev() { for (int i = 0; i < 2; ++i) if (e[i]) (void)hipEventDestroy(e[i]); } } eguard{ev};
   for (int i = 0; i < 2; ++i) HIP_TRY(hipEventCreateWithFlags(&ev[i], hipEventDisableTiming));
+  // Graph replay: a block's cached steps differ only in the tokens they read, so the
+  // first one is captured (every kernel of the step, on this stream) and replayed for the
+  // rest; the executable graphs live until the end of the call.
+  std::vector<hipGraphExec_t> execs;
+  struct Ex {
+    std::vector<hipGraphExec_t>* v;
+    hipStream_t s;
+    ~Ex() {
+      if (v->empty()) return;
+      (void)hipStreamSynchronize(s);  // no replay may still be pending (error paths too)
+      for (auto e : *v) (void)hipGraphExecDestroy(e);
+    }
+  } exguard{&execs, hs};
   const double t_start = now_ms();
   double ms_ref = 0, ms_step = 0;
   int steps = 0, refreshes = 0, wasted = 0;
   for (int b = 0; b < d.nblocks; ++b) {
     int issued = 0;  // steps of this block enqueued (the first fused with the refresh)
+    hipGraphExec_t exec = nullptr;
     auto issue = [&]() -> dllm_status {
       const bool full = issued == 0 || d.mode == DLLM_CACHE_NONE;
-      dllm_status r = full ? do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr)
-                           : do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+      dllm_status r = DLLM_OK;
+      if (full) {
+        r = do_refresh_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+      } else if (!graphs) {
+        r = do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+      } else {
+        if (!exec) {
+          HIP_TRY(hipStreamBeginCapture(hs, hipStreamCaptureModeThreadLocal));
+          r = do_step(c, b, c.at<int>(w.nun), c.at<int>(w.rem), nullptr, nullptr, nullptr);
+          hipGraph_t g = nullptr;
+          const hipError_t e = hipStreamEndCapture(hs, &g);
+          if (!r && e != hipSuccess) r = fail(DLLM_E_HIP, "stream capture: %s", hipGetErrorString(e));
+          if (!r) {
+            const hipError_t ei = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+            if (ei != hipSuccess) r = fail(DLLM_E_HIP, "graph instantiate: %s", hipGetErrorString(ei));
+            else execs.push_back(exec);
+          }
+          if (g) (void)hipGraphDestroy(g);
+        }
+        if (!r) HIP_TRY(hipGraphLaunch(exec, hs));
+      }
       if (r) return r;
       const int slot = issued & 1;
       HIP_TRY(hipMemcpyAsync(host + slot * d.B, c.at<int>(w.rem), d.B * sizeof(int32_t),
@@ -676,6 +723,16 @@ dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm
     out->speculative_steps = wasted;
   }
   return DLLM_OK;
+}
+
+dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s, dllm_stream_t stream,
+                          dllm_stats* out) {
+  return generate_impl(m, s, stream, false, out);
+}
+
+dllm_status dllm_generate_graphs(const dllm_model_desc* m, const dllm_seq_desc* s,
+                                 dllm_stream_t stream, dllm_stats* out) {
+  return generate_impl(m, s, stream, true, out);
 }
 
 // ---------------------------------------------------------------- kernel-level entries

@@ -172,10 +172,13 @@ class Session:
         out.update(logits=lg, conf=conf, argmax=arg)
         return out
 
-    def generate(self, stream=None):
+    def generate(self, stream=None, graphs: bool = False):
+        """Whole generation (dllm_generate; with graphs, dllm_generate_graphs: each
+        block's cached steps replayed from a captured HIP graph)."""
         spb = (C.c_int32 * max(1, self.n_blocks))()
         st = bd.Stats(steps_per_block=spb)
-        self.lib.call("dllm_generate", *self._args(), bd.stream_handle(stream), C.byref(st))
+        self.lib.call("dllm_generate_graphs" if graphs else "dllm_generate", *self._args(),
+                      bd.stream_handle(stream), C.byref(st))
         stats = {"steps": st.steps, "refreshes": st.refreshes, "tokens": st.tokens,
                  "blocks": st.blocks, "ms_total": st.ms_total, "ms_refresh": st.ms_refresh,
                  "ms_step": st.ms_step, "steps_per_block": list(spb)[: self.n_blocks],

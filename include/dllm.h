@@ -193,6 +193,14 @@ dllm_status dllm_refresh_step(const dllm_model_desc* m, const dllm_seq_desc* s, 
 dllm_status dllm_generate(const dllm_model_desc* m, const dllm_seq_desc* s,
                           dllm_stream_t stream, dllm_stats* out);
 
+/* dllm_generate with each block's cached steps replayed from a HIP graph: the block's
+ * first cached step is captured on `stream` (its kernels only; the per-step 4*batch-byte
+ * read stays outside) and replayed for the block's later steps.  Same kernels, same
+ * results as dllm_generate, bit for bit.  DLLM_E_UNSUPPORTED while a kernel class is
+ * being timed (dllm_profile_select): its events cannot be recorded inside a graph.    */
+dllm_status dllm_generate_graphs(const dllm_model_desc* m, const dllm_seq_desc* s,
+                                 dllm_stream_t stream, dllm_stats* out);
+
 /* Cache staleness: how far the block-wise approximate cache is from the exact K/V of
  * the current tokens.  [A] 1.1 checks that the K/V activations of adjacent steps have a
  * cosine similarity close to 1 and [B] "Core innovation" shows the same similarity;

@@ -323,6 +323,41 @@ def test_generate_matches_the_step_by_step_loop(lib, mode, tau):
     print(f"steps per block {spb}, speculative steps {st['speculative_steps']}")
 
 
+@pytest.mark.parametrize("mode,tau", [("dual", 0.9), ("dual", 0.3), ("prefix", 0.9)])
+def test_graph_replay_generate_matches_eager(lib, mode, tau):
+    """dllm_generate_graphs replays each block's captured cached step; every replay is
+    followed by the host's read of the step's outcome, and every step's decisions feed
+    the next: tokens and steps per block must equal the eager loop's, bit for bit, over
+    two runs (the second reuses nothing: graphs live for one call)."""
+    wl = small_bf16(Hq=2, Hkv=1, mode=mode, B=2, K=16, P=40)
+    model = gpu_model(lib, wl)
+    prompt = synth.make_prompt(wl)
+    e = Session(model, prompt, wl.gen_len, wl.block_len, tau, mode)
+    want, st_e = e.generate()
+    for _ in range(2):
+        g = Session(model, prompt, wl.gen_len, wl.block_len, tau, mode)
+        got, st_g = g.generate(graphs=True)
+        assert np.array_equal(got, want)
+        assert st_g["steps_per_block"] == st_e["steps_per_block"]
+        assert st_g["steps"] == st_e["steps"]
+
+
+def test_graph_replay_generate_matches_eager_llada_shape(lib):
+    """The 8B LLaDA shape (weights made on the device), DualCache, two blocks."""
+    wl = replace(synth.WORKLOADS["llada8b_dual_p1000_g1024"], gen_len=64)
+    wl = synth.with_scale(wl, 20.0)
+    model = Model.synthetic(lib, wl)
+    prompt = synth.make_prompt(wl)
+    out = []
+    for graphs in (False, True):
+        s = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
+        toks, st = s.generate(graphs=graphs)
+        out.append((toks, st["steps_per_block"]))
+    assert np.array_equal(out[0][0], out[1][0]) and out[0][1] == out[1][1]
+    del model
+    torch.cuda.empty_cache()
+
+
 FULL_SIZE = ["llada8b_dual_p1000_g1024", "llada8b_prefix_p256_g256", "dream7b_dual_b8_p512_g512"]
 
 
