@@ -33,8 +33,11 @@ float64 library routines; RoPE against its closed form (norm preservation, relat
 position property, position 0 identity); full forward against an independent torch
 float64 re-composition; first cached step after a refresh equals the full forward
 (both cache modes); refreshing before every step reproduces the no-cache algorithm;
-layer-0 K/V of unchanged tokens equal fresh ones.  Later cached steps are defined by
-the cache-staleness reading only: parity unpinned beyond those invariants.
+layer-0 K/V of unchanged tokens equal fresh ones; with an empty prompt every prefix-mode
+step of block 0 recomputes all rows, so each of them (not only the first) equals the full
+forward, while DualCache drifts from the second step on (pins the suffix recompute of
+prefix mode).  Later DualCache steps are defined by the cache-staleness reading only:
+beyond those invariants their values have no external pin.
 """
 from __future__ import annotations
 

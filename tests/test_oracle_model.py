@@ -213,3 +213,39 @@ def test_refresh_before_every_step_is_the_no_cache_algorithm():
             s.refresh()
             s.step(b)
     np.testing.assert_array_equal(s.tokens[:, s.P:], ref)
+
+
+def test_prefix_mode_with_empty_prompt_is_the_full_forward_at_every_step():
+    """Prefix-mode caching keeps only the positions before the block and recomputes the
+    block together with everything after it on every step (ccyt168.com Fast-dLLM
+    article, section 1.1: the prefix cache against DualCache, which also keeps the
+    masked suffix; techwalker.com explainer, "Core innovation").  With an empty prompt
+    and block 0, nothing comes from the cache at all, so every cached step of the block
+    (not only the first) must equal the no-cache full forward of the current tokens.
+    DualCache keeps the stale suffix K/V instead, so from the second step on its logits
+    move away from the full forward.  A prefix step that recomputed only the block rows
+    would behave like DualCache here and fail the first assertion."""
+    wl = replace(small_workload(), prompt_len=0, gen_len=12, block_len=4, cache_mode="prefix")
+    M = om.OracleModel(wl)
+    prompt = np.zeros((wl.batch, 0), dtype=np.int64)
+    # tau > 1: one token per step, so block 0 takes 4 steps
+    s = Session(M, prompt, wl.gen_len, wl.block_len, 1.5, "prefix")
+    d = Session(M, prompt, wl.gen_len, wl.block_len, 1.5, "dual")
+    s.refresh()
+    d.refresh()
+    s0, s1 = s.block_span(0)
+    assert (s0, s1) == (0, 4)
+    n = 0
+    while not s.block_done(0):
+        n += 1
+        d.tokens[...] = s.tokens           # both modes see the same token state
+        _, ref = om.full_forward(M, s.tokens, logit_rows=slice(s0, s1))
+        got_dual = om.cached_step(M, d.tokens, d.cache, s0, s1, "dual")
+        out = s.step(0)
+        np.testing.assert_allclose(out["logits"], ref, rtol=1e-11, atol=1e-11)
+        dual_err = np.max(np.abs(got_dual - ref))
+        if n == 1:
+            assert dual_err < 1e-11           # property (a): both exact after a refresh
+        else:
+            assert dual_err > 1e-3, f"step {n}: DualCache should read a stale suffix"
+    assert n == 4
