@@ -3,6 +3,13 @@ protocol for decisions taken from floating-point confidences."""
 import numpy as np
 
 import synth
+from oracle import decode
+
+# Bound on |GPU confidence - oracle confidence| for the fp32 (tiny) model, asserted by the
+# fp32 teacher-forced and refresh-step tests and relied on by the free-running ones: the
+# fp32 logits agree to about 1e-6 relative (|logit| < ~20), so a confidence c moves by at
+# most c (exp(2 dl) - 1) ~ 4e-5 c, plus the fp32 rounding of the exp-sum.
+CONF_TOL_F32 = 2e-5
 
 
 def dev_bf16(bits: np.ndarray, device="cuda"):
@@ -83,3 +90,41 @@ def safe_sequences(conf_ref, conf_unc, tau, masked):
             if c[order[0]] - c[order[1]] <= u[order[0]] + u[order[1]]:
                 ok[b] = False
     return ok
+
+
+def grade_confidence_stage(logits_rows, gconf, garg, mask_id, rel=2e-5):
+    """Per-stage grading of the confidence pass (max softmax probability, argmax with the
+    mask id excluded): the oracle's definition applied to the very logits the GPU
+    produced.  The maximum of identical fp32 values is exact, so the argmax (lowest id on
+    ties) must match on every row; the confidence differs only by the fp32 rounding of
+    the exp-sum.  Returns the largest relative confidence difference."""
+    rc, ra = decode.confidence_argmax(np.asarray(logits_rows, np.float64), mask_id)
+    garg = np.asarray(garg).reshape(-1)
+    gconf = np.asarray(gconf, np.float64).reshape(-1)
+    assert np.array_equal(garg, ra), f"argmax differs on rows {np.nonzero(garg != ra)[0][:8]}"
+    d = float(np.max(np.abs(gconf - rc) / rc))
+    assert d < rel, f"confidence rel diff {d}"
+    return d
+
+
+def grade_unmask_stage(before, gconf, garg, gtok, gnun, grem, mask_id, tau, gidx=None):
+    """Per-stage grading of the threshold unmask: the oracle's rule applied to the GPU's
+    own confidences and argmaxes must give the GPU's tokens, unmask counts and masks left
+    bit for bit on every sequence (pure compare-and-index work; the threshold is compared
+    in fp32 on both sides, as the kernel does).  Returns the unmask set U [B, K]."""
+    before = np.asarray(before)
+    B, K = before.shape
+    tau32 = float(np.float32(tau))
+    conf = np.asarray(gconf, np.float32).astype(np.float64).reshape(B, K)
+    arg = np.asarray(garg).reshape(B, K)
+    want, U, wn, wr = decode.unmask(before, conf, arg, mask_id, tau32)
+    assert np.array_equal(np.asarray(gtok).reshape(B, K), want), "tokens differ"
+    assert np.array_equal(np.asarray(gnun).reshape(B), wn), "n_unmasked differs"
+    assert np.array_equal(np.asarray(grem).reshape(B), wr), "remaining differs"
+    if gidx is not None:
+        gidx = np.asarray(gidx).reshape(B, K)
+        for b in range(B):
+            sel = np.nonzero(U[b])[0]
+            assert np.array_equal(gidx[b, :len(sel)], sel), f"unmasked_idx of sequence {b}"
+            assert np.all(gidx[b, len(sel):] == -1)
+    return U
