@@ -78,6 +78,8 @@ _SIGS = {
                                          C.c_size_t, _P]),
     "dllm_kernel_confidence_unmask": (_I, [_P, _I, _I, _I, _I, _I, C.c_float, _P, _I, _P, _P, _P,
                                            _P, _P, _P, C.c_size_t, _P]),
+    "dllm_kernel_confidence_unmask_noalloc": (_I, [_P, _I, _I, _I, _I, _I, C.c_float, _P, _I, _P,
+                                                   _P, _P, _P, _P, _P]),
     "dllm_linear_workspace_bytes": (C.c_size_t, [_I, _I, _I, _I]),
     "dllm_kernel_linear": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, C.c_float, _P, C.c_size_t, _P]),
     "dllm_status_string": (C.c_char_p, [_I]),

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -802,6 +803,72 @@ dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dty
   float* pm = (float*)base;
   float* ps_ = (float*)(base + up(p.part_elems * 4));
   int* pi = (int*)(base + 2 * up(p.part_elems * 4));
+  ProfScope ps(DLLM_K_CONF_UNMASK, st);
+  HIP_TRY(launch_conf_unmask(logits_dtype, p, logits, B, K, V, mask_id, tau, tokens_block,
+                             ld_tokens, conf, argmax, n_unmasked, remaining, unmasked_idx, pm, ps_,
+                             pi, st));
+  return DLLM_OK;
+}
+
+// ---------------------------------------------------------------- no-allocation entry
+// For callers that cannot allocate (code under graph capture, tight serving loops): the
+// confidence pass's slice partials live in one file-scope device array per GPU instead
+// of a caller workspace.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): its device address is looked up once per
+// device with that device current and kept.
+namespace {
+constexpr size_t kScratchParts = 65536;  // (max, sum, argmax) slice triples: 768 KiB
+static __device__ __align__(256) float scratch[3 * kScratchParts];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dllm_status scratch_for(hipStream_t st, char** out) {
+  int cur = 0;
+  HIP_TRY(hipGetDevice(&cur));
+  int dev = cur;
+  if (st != nullptr) HIP_TRY(hipStreamGetDevice(st, &dev));
+  if (dev != cur)
+    return fail(DLLM_E_ARG, "stream belongs to device %d, the current device is %d", dev, cur);
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLLM_E_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr) return fail(DLLM_E_HIP, "no device address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = (char*)g_scratch_ptr[dev];
+  return DLLM_OK;
+}
+}  // namespace
+
+dllm_status dllm_kernel_confidence_unmask_noalloc(const void* logits, int32_t logits_dtype,
+                                                  int32_t B, int32_t K, int32_t V,
+                                                  int32_t mask_id, float tau,
+                                                  int32_t* tokens_block, int32_t ld_tokens,
+                                                  float* conf, int32_t* argmax,
+                                                  int32_t* n_unmasked, int32_t* remaining,
+                                                  int32_t* unmasked_idx, dllm_stream_t stream) {
+  if (!logits || !tokens_block || !conf || !argmax || !n_unmasked || !remaining)
+    return fail(DLLM_E_NULL, "a required pointer is NULL");
+  if (logits_dtype != DLLM_F32 && logits_dtype != DLLM_BF16) return fail(DLLM_E_ARG, "bad dtype");
+  if (B < 1 || K < 1 || V < 2 || ld_tokens < K) return fail(DLLM_E_SHAPE, "bad sizes");
+  if (K > 64) return fail(DLLM_E_UNSUPPORTED, "K > 64");
+  if (mask_id < 0 || mask_id >= V) return fail(DLLM_E_ARG, "mask_id outside [0, V)");
+  if (std::isnan(tau)) return fail(DLLM_E_ARG, "tau is NaN");
+  ConfPlan p = conf_plan(B * K, V, B);
+  if (p.part_elems > kScratchParts)
+    return fail(DLLM_E_UNSUPPORTED, "needs %zu slice partials, the static scratch holds %zu",
+                p.part_elems, kScratchParts);
+  hipStream_t st = (hipStream_t)stream;
+  char* base = nullptr;
+  dllm_status s = scratch_for(st, &base);
+  if (s) return s;
+  // every (row, slice) triple is written by pass 1 before pass 2 reads it: nothing to clear
+  float* pm = (float*)base;
+  float* ps_ = pm + kScratchParts;
+  int* pi = (int*)(pm + 2 * kScratchParts);
   ProfScope ps(DLLM_K_CONF_UNMASK, st);
   HIP_TRY(launch_conf_unmask(logits_dtype, p, logits, B, K, V, mask_id, tau, tokens_block,
                              ld_tokens, conf, argmax, n_unmasked, remaining, unmasked_idx, pm, ps_,

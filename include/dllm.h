@@ -256,6 +256,24 @@ dllm_status dllm_kernel_confidence_unmask(const void* logits, int32_t logits_dty
                                           int32_t* remaining, int32_t* unmasked_idx, void* ws,
                                           size_t ws_bytes, dllm_stream_t stream);
 
+/* dllm_kernel_confidence_unmask for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation and outputs, with the slice partials in a static device array of the
+ * library instead of a workspace (768 KiB per GPU the library runs on, held until the
+ * process ends; its address is looked up on the first call on each device).  Allocates
+ * nothing and calls no allocating routine.  DLLM_E_UNSUPPORTED when the pass needs more
+ * than 65536 slice partials (B * K rows times the slices per row; at most 2048 per
+ * sequence, so any B <= 32 fits); DLLM_E_ARG if `stream` belongs to another device than
+ * the current one.  Every call on one GPU shares that array: calls that overlap on one
+ * GPU (two streams, or two threads) race and must be serialised by the caller.       */
+dllm_status dllm_kernel_confidence_unmask_noalloc(const void* logits, int32_t logits_dtype,
+                                                  int32_t B, int32_t K, int32_t V,
+                                                  int32_t mask_id, float tau,
+                                                  int32_t* tokens_block, int32_t ld_tokens,
+                                                  float* conf, int32_t* argmax,
+                                                  int32_t* n_unmasked, int32_t* remaining,
+                                                  int32_t* unmasked_idx, dllm_stream_t stream);
+
 /* y = x W^T for x T [M][K], W T [N][K].  mode 0: y T [M][N]; mode 1: y fp32 [M][N] =
  * scale * x W^T; mode 2: y fp32 [M][N] += x W^T (residual add).  Same kernels as the
  * model path (MFMA for DLLM_BF16: K % 256 == 0, N % 8 == 0; fp32: K % 16 == 0).  ws from
