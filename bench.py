@@ -86,6 +86,43 @@ def kernel_work(cls: str, wl, R_step: int):
     return table[cls]
 
 
+def layer_params(m) -> int:
+    """Weights of one transformer layer (QKV, O, gate/up, down; norms are negligible)."""
+    return ((m.n_heads + 2 * m.n_kv_heads) * m.head_dim * m.d_model
+            + m.d_model * m.n_heads * m.head_dim + 3 * m.d_ffn * m.d_model)
+
+
+def generation_roofline(wl, n_refresh: int, n_steps: int, seconds: float):
+    """Roofline time of one whole generation from its measured NFE, against the measured
+    wall time.  Algorithmic work only (what the method must move or compute):
+      * a refresh is the full forward over all S rows, bound by the larger of its MFMA
+        time, 2 B S (layer params) L + 4 B S^2 Hq D L flops at the bf16 peak, and its HBM
+        time (layer weights once plus the K/V it writes);
+      * a cached step reads every layer's weights, the LM head and the whole K/V cache
+        once (HBM-bound at one block of rows);
+      * each block's first step is fused with its refresh here: on top of the refresh it
+        needs the last layer's weights and the LM head once more.
+    T_roof = n_refresh (refresh + fused-step tail) + (n_steps - n_refresh) cached steps."""
+    m = wl.model
+    B, S, L, e = wl.batch, wl.seq_len, m.n_layers, 2 if m.dtype == "bf16" else 4
+    P = layer_params(m)
+    head = m.vocab * m.d_model
+    kv = L * 2 * B * m.n_kv_heads * S * m.head_dim * e
+    f_ref = 2.0 * B * S * P * L + 4.0 * B * S * S * m.n_heads * m.head_dim * L
+    b_ref = P * L * e + kv
+    t_ref = max(f_ref / (PEAK_BF16_TFLOPS * 1e12), b_ref / (PEAK_HBM_GBS * 1e9))
+    b_step = (P * L + head) * e + kv
+    t_step = b_step / (PEAK_HBM_GBS * 1e9)
+    t_tail = (P + head) * e / (PEAK_HBM_GBS * 1e9)
+    n_cached = n_steps - n_refresh
+    t_roof = n_refresh * (t_ref + t_tail) + n_cached * t_step
+    return {"t_roof_s": round(t_roof, 4), "t_s": round(seconds, 4),
+            "frac": round(t_roof / seconds, 4),
+            "refresh_roof_ms": round(t_ref * 1e3, 3), "refresh_tflop": round(f_ref / 1e12, 2),
+            "step_roof_ms": round(t_step * 1e3, 3), "step_gb": round(b_step / 1e9, 3),
+            "n_refresh": n_refresh, "n_cached_steps": n_cached}
+
+
 def counters_for(cls: str, wl_name: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel sources."""
@@ -114,17 +151,30 @@ def source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int):
-    """The oracle (float64, as it stands) on a bounded sample of the workload: one full
-    layer over all S rows (a refresh layer) and one layer over the block rows against the
-    cache plus the LM head and the confidence/unmask rule (a step).  Scaled by the layer
-    count and combined with the GPU run's NFE into generated tokens/s."""
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int, repeats: int = 3):
+    """The oracle as it stands, in float32 with bf16 rounding at its storage points (its
+    timed mode for bf16 models), on a bounded sample of the workload: one full layer over
+    all S rows (a refresh layer) and one cached-step layer over the block rows against the
+    cache, plus the LM head and the confidence/unmask rule, each run ``repeats`` times
+    (the fastest kept).  Scaled by the layer count and combined with the GPU run's NFE
+    into generated tokens/s (extrapolated)."""
     from threadpoolctl import threadpool_info
     from oracle import decode
     from oracle import model as om
     m = wl.model
+    dt = np.float32 if m.dtype == "bf16" else np.float64
     wl1 = replace(wl, model=replace(m, n_layers=1))
-    M = om.OracleModel(wl1, dtype=np.float64)
+    M = om.OracleModel(wl1, dtype=dt)
     for n in ("embed", "final_norm", "lm_head"):
         M.w(n)
     for n in ("attn_norm", "w_qkv", "w_o", "ffn_norm", "w_gate_up", "w_down"):
@@ -132,40 +182,57 @@ def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int):
     prompt = synth.make_prompt(wl1)
     B, P, S, K = wl.batch, wl.prompt_len, wl.seq_len, wl.block_len
     tokens = np.concatenate([prompt, np.full((B, wl.gen_len), m.mask_id, np.int64)], axis=1)
-    t0 = time.perf_counter()
-    x = om.embed(M, tokens)
-    q, k, v = om.layer_qkv(M, 0, x, np.arange(S))
-    om.layer_rest(M, 0, x, q, k, v)
-    t_ref_layer = time.perf_counter() - t0
-    cache = om.KVCache(1, B, m.n_kv_heads, S, m.head_dim, np.float64)
+
+    def best(f):
+        ts = []
+        out = None
+        for _ in range(repeats):
+            t0 = time.perf_counter()
+            out = f()
+            ts.append(time.perf_counter() - t0)
+        return min(ts), sum(ts), out
+
+    def ref_layer():
+        x = om.embed(M, tokens)
+        q, k, v = om.layer_qkv(M, 0, x, np.arange(S))
+        om.layer_rest(M, 0, x, q, k, v)
+        return k, v
+    t_ref_layer, spent, (k, v) = best(ref_layer)
+    cache = om.KVCache(1, B, m.n_kv_heads, S, m.head_dim, dt)
     cache.K[0][...] = k
     cache.V[0][...] = v
-    t0 = time.perf_counter()
-    logits = om.cached_step(M, tokens, cache, P, P + K, wl.cache_mode)
-    t_step_1 = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    conf, arg = decode.confidence_argmax(logits.reshape(B * K, -1), m.mask_id)
-    decode.unmask(tokens[:, P:P + K], conf.reshape(B, K), arg.reshape(B, K), m.mask_id,
-                  wl.threshold)
-    t_dec = time.perf_counter() - t0
+    t_step_1, sp, logits = best(lambda: om.cached_step(M, tokens, cache, P, P + K, wl.cache_mode))
+    spent += sp
+
+    def dec():
+        conf, arg = decode.confidence_argmax(logits.reshape(B * K, -1), m.mask_id)
+        decode.unmask(tokens[:, P:P + K], conf.reshape(B, K), arg.reshape(B, K), m.mask_id,
+                      wl.threshold)
+    t_dec, sp, _ = best(dec)
+    spent += sp
     # a 1-layer cached step = 1 layer + LM head; split the LM head off with a timed call
-    t0 = time.perf_counter()
-    om.lm_head(M, np.zeros((B, K, m.d_model)))
-    t_head = time.perf_counter() - t0
+    t_head, sp, _ = best(lambda: om.lm_head(M, np.zeros((B, K, m.d_model), dt)))
+    spent += sp
     t_step_layer = max(t_step_1 - t_head, 0.0)
     L = m.n_layers
     t_refresh = L * t_ref_layer
     t_step = L * t_step_layer + t_head + t_dec
     total = nfe_refreshes * t_refresh + nfe_steps * t_step
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                   if i.get("user_api") == "blas"] or [1])
+    prec = "float32 with bf16 rounding at the storage points" if dt == np.float32 else "float64"
     return {
         "value": round(B * wl.gen_len / total, 4), "unit": "tokens/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle float64, 1 of {L} layers timed: full-sequence layer {t_ref_layer:.2f} s, "
-                   f"cached-step layer {t_step_layer:.3f} s, LM head {t_head:.3f} s, decode "
-                   f"{t_dec:.3f} s; scaled x{L} and by the GPU run's NFE ({nfe_steps} steps, "
+        "sample": (f"oracle in {prec}, 1 of {L} layers timed (best of {repeats}): "
+                   f"full-sequence layer {t_ref_layer:.2f} s, cached-step layer "
+                   f"{t_step_layer:.3f} s, LM head {t_head:.3f} s, decode {t_dec:.3f} s; "
+                   f"scaled x{L} and by the GPU run's NFE ({nfe_steps} steps, "
                    f"{nfe_refreshes} refreshes); extrapolated"),
-        "sample_seconds": round(t_ref_layer + t_step_1 + t_dec + t_head, 2),
+        "sample_seconds": round(spent, 2),
+        "host_cpus": os.cpu_count(), "cpu_model": host_cpu_model(),
+        "blas_threads": threads,
+        "openblas_num_threads_env": os.environ.get("OPENBLAS_NUM_THREADS"),
     }
 
 
@@ -369,6 +436,11 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="also run plain device copies of this many MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counter scale)")
+    ap.add_argument("--stage", choices=["refresh", "step"], default=None,
+                    help="time one stage at the workload's full shape instead of whole "
+                         "generations: after a prefill, --repeat refreshes, or --repeat cached "
+                         "steps of block 0 (for counter runs), one JSON line")
+    ap.add_argument("--repeat", type=int, default=10)
     ap.add_argument("--roofline-kernel", default="auto")
     ap.add_argument("--profile-every", type=int, default=7,
                     help="time one launch in N of the roofline kernel class")
@@ -414,6 +486,22 @@ def main():
     if a.ablation:
         del sess
         print(json.dumps({"ablation": ablation(model, wl, torch)}), flush=True)
+        return
+    if a.stage:
+        sess.prefill()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(a.repeat):
+            if a.stage == "refresh":
+                sess.refresh(0)
+            else:
+                sess.reset_tokens()
+                sess.step(0, logits=False)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / a.repeat * 1e3
+        log(f"{a.stage}: {ms:.3f} ms per call over {a.repeat}")
+        print(json.dumps({"stage": a.stage, "workload": wl.name, "ms_per_call": round(ms, 3),
+                          "repeat": a.repeat}), flush=True)
         return
     if a.staleness:
         print(json.dumps({"staleness": staleness_trace(sess, wl, a.staleness)}), flush=True)
@@ -469,6 +557,8 @@ def main():
     toks = wl.batch * wl.gen_len * a.steps
     value = toks / dt
     nfe_steps, nfe_ref = stats[-1]["steps"], stats[-1]["refreshes"]
+    gen_roof = generation_roofline(wl, nfe_ref, nfe_steps, dt / a.steps) \
+        if wl.cache_mode != "none" else None
     R_step = wl.block_len if wl.cache_mode == "dual" else wl.gen_len
     flops, bytes_ = kernel_work(cls, wl, R_step)
     avg_s = tot_ms.value / 1e3 / max(1, n_launch.value)
@@ -496,8 +586,11 @@ def main():
                    "gen_len": wl.gen_len, "block_len": wl.block_len, "cache": wl.cache_mode,
                    "threshold": wl.threshold, "logit_scale": round(wl.model.logit_scale, 4),
                    "nfe_steps": nfe_steps, "nfe_refreshes": nfe_ref,
-                   "tokens_per_step": round(wl.batch * wl.gen_len / max(1, nfe_steps), 3)},
+                   "tokens_per_step": round(wl.batch * wl.gen_len / max(1, nfe_steps), 3),
+                   "unmask_fraction_per_step": round(
+                       wl.batch * wl.gen_len / max(1, stats[-1]["masked_at_step_start"]), 4)},
         "roofline": roof,
+        "generation_roofline": gen_roof,
     }
     if not a.no_kernels:
         log("kernel-only rates (attention, confidence)")

@@ -50,7 +50,7 @@ class Stats(C.Structure):
     _fields_ = [("steps", C.c_int32), ("refreshes", C.c_int32), ("tokens", C.c_int32),
                 ("blocks", C.c_int32), ("ms_total", C.c_double), ("ms_refresh", C.c_double),
                 ("ms_step", C.c_double), ("steps_per_block", C.POINTER(C.c_int32)),
-                ("speculative_steps", C.c_int32)]
+                ("speculative_steps", C.c_int32), ("masked_at_step_start", C.c_int64)]
 
 
 class DllmError(RuntimeError):
@@ -67,7 +67,7 @@ _SIGS = {
     "dllm_prefill_cache": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _P]),
     "dllm_refresh_cache": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P]),
     "dllm_cache_staleness": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, C.c_size_t,
-                                  _P, _P]),
+                                  _P, C.POINTER(C.c_double), _P]),
     "dllm_block_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P, _P]),
     "dllm_refresh_step": (_I, [C.POINTER(ModelDesc), C.POINTER(SeqDesc), _I, _P, _P, _P, _P, _P,
                                _P]),

@@ -10,6 +10,8 @@
 #include <string>
 #include <vector>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "../../include/dllm.h"
 #include "../../include/dllm_synth.h"
 #include "kernels.h"
@@ -72,6 +74,13 @@ struct ProfScope {
     (void)hipEventRecord(g_prof.ev[g_prof.used + 1], st);
     g_prof.used += 2;
   }
+};
+
+// Host-side roctx range around the enqueue of one stage (prefill, refresh, a step), so a
+// profiler's marker trace shows which kernels each stage launched.
+struct Range {
+  explicit Range(const char* name) { roctxRangePushA(name); }
+  ~Range() { roctxRangePop(); }
 };
 
 // ------------------------------------------------------------------ shapes
@@ -392,6 +401,7 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh, int l0 = 0) {
 }
 
 dllm_status do_refresh(const Ctx& c) {
+  Range r("dllm refresh");
   dllm_status st = run_layers(c, 0, c.d.S, true);
   c.pend = Pending{};  // the last layer's tail is skipped: nothing is pending
   c.rs = RowScale{};
@@ -442,6 +452,7 @@ dllm_status decode_tail(const Ctx& c, int b, int R, int* n_un, int* rem, float* 
 
 dllm_status do_step(const Ctx& c, int b, int* n_un, int* rem, float* logits, float* conf,
                     int* argmax) {
+  Range r("dllm step");
   const Dims& d = c.d;
   const int R = step_rows(d, b);
   dllm_status st = run_layers(c, d.P + b * d.K, R, false);
@@ -462,6 +473,7 @@ bool refresh_step_fits(const Dims& d) {
 // the block-row recompute of layers 0 .. L-2 that a separate first step would do.
 dllm_status do_refresh_step(const Ctx& c, int b, int* n_un, int* rem, float* logits,
                             float* conf, int* argmax) {
+  Range r(b == 0 ? "dllm prefill+step" : "dllm refresh+step");
   const Dims& d = c.d;
   dllm_status st = (b == 0) ? do_init(c) : DLLM_OK;
   if (st) return st;
@@ -516,6 +528,7 @@ dllm_status dllm_prefill_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
   dllm_status st = setup(m, s, &d, &w);
   if (st) return st;
   Ctx c{d, m, s, w, (char*)s->workspace, (hipStream_t)stream};
+  Range r("dllm prefill");
   st = do_init(c);
   if (st) return st;
   return do_refresh(c);
@@ -534,7 +547,7 @@ dllm_status dllm_refresh_cache(const dllm_model_desc* m, const dllm_seq_desc* s,
 
 dllm_status dllm_cache_staleness(const dllm_model_desc* m, const dllm_seq_desc* s, int32_t block,
                                  void* fresh_cache, size_t fresh_bytes, float* out,
-                                 dllm_stream_t stream) {
+                                 double* reuse, dllm_stream_t stream) {
   Dims d;
   Ws w;
   dllm_status st = setup(m, s, &d, &w);
@@ -559,6 +572,7 @@ dllm_status dllm_cache_staleness(const dllm_model_desc* m, const dllm_seq_desc* 
   // the block's (DualCache), those before the block (prefix)
   const int s0 = d.P + block * d.K;
   const int x1 = (d.mode == DLLM_CACHE_PREFIX) ? d.S : s0 + d.K;
+  if (reuse) *reuse = (double)(d.S - (x1 - s0)) / d.S;
   HIP_TRY(launch_staleness(d.dtype, s->kv_cache, fresh_cache, d.L, d.B, d.Hkv, d.S, d.Sp, d.D,
                            s0, x1, cf.at<double>(w.logits), out, (hipStream_t)stream));
   return DLLM_OK;
@@ -645,6 +659,7 @@ static dllm_status generate_impl(const dllm_model_desc* m, const dllm_seq_desc* 
   const double t_start = now_ms();
   double ms_ref = 0, ms_step = 0;
   int steps = 0, refreshes = 0, wasted = 0;
+  int64_t masked_seen = 0;  // masked block positions at the start of each step, summed
   for (int b = 0; b < d.nblocks; ++b) {
     int issued = 0;  // steps of this block enqueued (the first fused with the refresh)
     hipGraphExec_t exec = nullptr;
@@ -683,12 +698,18 @@ static dllm_status generate_impl(const dllm_model_desc* m, const dllm_seq_desc* 
     st = issue();
     if (st) return st;
     int confirmed = 0;  // steps whose outcome has been read
+    int64_t masked_now = (int64_t)d.B * d.K;  // every block starts fully masked
     for (;;) {
       const int slot = confirmed & 1;
       HIP_TRY(hipEventSynchronize(ev[slot]));
       ++confirmed;
+      masked_seen += masked_now;
       int left = 0;
-      for (int i = 0; i < d.B; ++i) left = std::max(left, (int)host[slot * d.B + i]);
+      masked_now = 0;
+      for (int i = 0; i < d.B; ++i) {
+        left = std::max(left, (int)host[slot * d.B + i]);
+        masked_now += host[slot * d.B + i];
+      }
       if (confirmed == 1) {
         ms_ref += now_ms() - t0;
         t0 = now_ms();
@@ -722,6 +743,7 @@ static dllm_status generate_impl(const dllm_model_desc* m, const dllm_seq_desc* 
     out->ms_refresh = ms_ref;
     out->ms_step = ms_step;
     out->speculative_steps = wasted;
+    out->masked_at_step_start = masked_seen;
   }
   return DLLM_OK;
 }

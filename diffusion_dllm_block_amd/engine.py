@@ -149,14 +149,13 @@ class Session:
         dev = self.tokens.device
         fresh = torch.empty_like(self.cache)
         out = torch.empty((self.model.shape.n_layers, 2, 2), dtype=torch.float32, device=dev)
+        reuse = C.c_double()
         self.lib.call("dllm_cache_staleness", *self._args(), block, bd.ptr(fresh),
-                      fresh.numel(), bd.ptr(out), bd.stream_handle(stream))
+                      fresh.numel(), bd.ptr(out), C.byref(reuse), bd.stream_handle(stream))
         torch.cuda.synchronize(dev)
         o = out.cpu().numpy()
-        s0 = self.P + block * self.K
-        reused = (self.S - self.K) if self.mode == bd.CACHE_DUAL else s0
         return {"k_mean": o[:, 0, 0], "k_min": o[:, 0, 1], "v_mean": o[:, 1, 0],
-                "v_min": o[:, 1, 1], "reuse": reused / self.S}
+                "v_min": o[:, 1, 1], "reuse": reuse.value}
 
     def _decode(self, entry: str, block: int, logits: bool, stream) -> dict:
         torch = _torch()
@@ -182,7 +181,8 @@ class Session:
         stats = {"steps": st.steps, "refreshes": st.refreshes, "tokens": st.tokens,
                  "blocks": st.blocks, "ms_total": st.ms_total, "ms_refresh": st.ms_refresh,
                  "ms_step": st.ms_step, "steps_per_block": list(spb)[: self.n_blocks],
-                 "speculative_steps": st.speculative_steps}
+                 "speculative_steps": st.speculative_steps,
+                 "masked_at_step_start": st.masked_at_step_start}
         return self.tokens[:, self.P:].cpu().numpy(), stats
 
     def reset_tokens(self, prompt=None):

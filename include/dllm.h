@@ -136,6 +136,9 @@ typedef struct {
   int32_t* steps_per_block;           /* optional host array [gen_len/block_len], or NULL */
   int32_t speculative_steps;          /* steps queued ahead that found the block already
                                          finished (decode nothing; not in `steps`)       */
+  int64_t masked_at_step_start;       /* masked block positions when each step began,
+                                         summed over steps and sequences: tokens divided
+                                         by it is the mean fraction unmasked per step    */
 } dllm_stats;
 
 /* Sizes (host only, no device work).  Return 0 if the descriptors are invalid.       */
@@ -212,11 +215,14 @@ dllm_status dllm_generate_graphs(const dllm_model_desc* m, const dllm_seq_desc* 
  * block; prefix mode: the positions before it), averaged and minimised.  A vector pair
  * with both norms zero counts 1, with one zero norm 0.
  *   out: device float [n_layers][2][2] = {K mean, K min}, {V mean, V min}.
+ *   reuse: host double, may be NULL: the reuse ratio, the fraction of the S positions
+ *     whose K/V the step takes from the cache (DualCache (S - block_len) / S; prefix
+ *     mode s0 / S); written before the call returns.
  * tokens and kv_cache are not modified; the workspace is (as by any step).  Needs a
  * cache mode other than DLLM_CACHE_NONE and a prior dllm_prefill_cache.             */
 dllm_status dllm_cache_staleness(const dllm_model_desc* m, const dllm_seq_desc* s,
                                  int32_t block, void* fresh_cache, size_t fresh_bytes,
-                                 float* out, dllm_stream_t stream);
+                                 float* out, double* reuse, dllm_stream_t stream);
 
 /* ---- kernel-level entries (single stages on caller buffers) ---------------------- */
 

@@ -124,12 +124,12 @@ def test_staleness_validation(lib):
     s.kv_cache_bytes, s.workspace_bytes = cb, wb
     f = lib.cdll.dllm_cache_staleness
     for blk in (-1, 4):
-        assert f(C.byref(m), C.byref(s), blk, FAKE, cb, FAKE, None) == -6
-    assert f(C.byref(m), C.byref(s), 0, None, cb, FAKE, None) == -1
-    assert f(C.byref(m), C.byref(s), 0, FAKE, cb, None, None) == -1
-    assert f(C.byref(m), C.byref(s), 0, FAKE, cb - 1, FAKE, None) == -4
+        assert f(C.byref(m), C.byref(s), blk, FAKE, cb, FAKE, None, None) == -6
+    assert f(C.byref(m), C.byref(s), 0, None, cb, FAKE, None, None) == -1
+    assert f(C.byref(m), C.byref(s), 0, FAKE, cb, None, None, None) == -1
+    assert f(C.byref(m), C.byref(s), 0, FAKE, cb - 1, FAKE, None, None) == -4
     s.cache_mode = bd.CACHE_NONE
-    assert f(C.byref(m), C.byref(s), 0, FAKE, cb, FAKE, None) == -6
+    assert f(C.byref(m), C.byref(s), 0, FAKE, cb, FAKE, None, None) == -6
 
 
 def test_null_descriptors(lib):
