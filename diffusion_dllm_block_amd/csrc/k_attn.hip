@@ -59,9 +59,9 @@ __device__ __forceinline__ u32x4 mask8(const u32x4& v, int n) {
 
 // ============================================================================
 // Split-KV attention for a few query rows (a block step): grid (nchunk, Hq*nqt, B),
-// 4 waves, 32 query rows per workgroup.  Chunk c covers keys [c*4*kpw, (c+1)*4*kpw);
-// wave w walks its kpw keys in 32-key sub-tiles with an online softmax, loading the
-// next sub-tile while the current one is in the MFMAs.
+// NW waves (4 or 8), 32 query rows per workgroup.  Chunk c covers keys
+// [c*NW*kpw, (c+1)*NW*kpw); wave w walks its kpw keys in 32-key sub-tiles with an online
+// softmax, loading the next sub-tile while the current one is in the MFMAs.
 //
 // Products use v_mfma_f32_16x16x32_bf16 (lane l: A row l%16, k 8(l/16)..+7; B column
 // l%16, same k; C column l%16, rows 4(l/16)+r), so every operand load is 4 lanes x 16
@@ -73,8 +73,10 @@ __device__ __forceinline__ u32x4 mask8(const u32x4& v, int n) {
 //       lane's 8 scores are exactly its B operand, and the Vt operand of lane (d, j) is
 //       keys 8j .. 8j+7 of row d.
 // A query's 32 keys live in the 4 lanes l%16 + 16j, so its max and sum need two partner
-// combines (lane ^ 16, lane ^ 32).  Waves are merged through LDS in a fixed order; with several chunks the
-// workgroup writes unnormalised partials (O, m, l) and attn_combine merges them.
+// combines (lane ^ 16, lane ^ 32).  The waves are merged through LDS in a fixed order
+// (the upper half of the waves hands its rescaled O to the lower half, which adds it
+// and publishes the sums).  With several chunks the workgroup writes its unnormalised
+// chunk result (O, m, l) and attn_combine merges the chunks in chunk order.
 // ============================================================================
 constexpr int SK_OLD = HD + 4;  // LDS row stride (floats) of the per-wave O tiles
 constexpr int QS_LD = HD + 8;   // LDS row stride (elements) of the staged Q tile
@@ -99,32 +101,39 @@ __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
   for (int dt = 0; dt < 8; ++dt) t.v[dt] = load8_raw(vbase, 16 * dt + li, key0 + 8 * j, Sp);
 }
 
+// Chunk partial of one group: O [32][HD] unnormalised (scaled to the chunk maximum m),
+// then m [32] and l [32].
+constexpr int kPartStride = 32 * HD + 64;
+
 // ONE: every wave has a single 32-key sub-tile (nsub == 1): one operand tile in
 // registers, so two workgroups fit on a CU.
-template <bool ONE>
-__global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
+template <int NW, bool ONE>
+__global__ __launch_bounds__(NW * 64, ONE ? 2 : 1) void attn_splitkv_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
-    int Sp, int nqt, int nchunk, int nsub, float scale_log2, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
-  __shared__ float red_m[4][32], red_l[4][32];
-  __shared__ __attribute__((aligned(16))) float osum[4][32][SK_OLD];
+    int Sp, int nqt, int nchunk, int nsub, float scale_log2, float* __restrict__ part) {
+  constexpr int NT = NW * 64, NH = 4;  // NH: per-wave O slots in LDS
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  __shared__ float red_m[NW][32], red_l[NW][32];
+  __shared__ __attribute__((aligned(16))) float osum[NH][32][SK_OLD];
   const int chunk = blockIdx.x;
   const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
   const int hkv = hq / (Hq / Hkv);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, j = l >> 4;
   const int kpw = 32 * nsub;
-  const int wkey0 = chunk * 4 * kpw + w * kpw;
+  const int wkey0 = chunk * NW * kpw + w * kpw;
 
-  // The workgroup's Q tile (32 rows x 128) is read from memory once, two 16-byte pieces
-  // per thread (rows >= R clamped: computed, never stored), issued before the first K/Vt
-  // tile so that both are in flight together, then staged in LDS for the 4 waves.  The
-  // staging area is the start of osum, which is written only after the products.
+  // The workgroup's Q tile (32 rows x 128) is read from memory once, 512 16-byte pieces
+  // over the workgroup (rows >= R clamped: computed, never stored), issued before the
+  // first K/Vt tile so that both are in flight together, then staged in LDS for the
+  // waves.  The staging area is the start of osum, which is written only after the
+  // products.
+  constexpr int QP = 512 / NT;  // Q pieces per thread
   const uint16_t* qh = q + ((int64_t)b * Hq + hq) * R * HD;
-  u32x4 qg[2];
+  u32x4 qg[QP];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = threadIdx.x + 256 * u;
+  for (int u = 0; u < QP; ++u) {
+    const int e = threadIdx.x + NT * u;
     qg[u] = *reinterpret_cast<const u32x4*>(qh + (int64_t)min(qt * 32 + (e >> 4), R - 1) * HD +
                                             8 * (e & 15));
   }
@@ -134,8 +143,8 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
   load_kv16(ta, kbase, vbase, wkey0, li, j, S, Sp);
   uint16_t* qs = reinterpret_cast<uint16_t*>(&osum[0][0][0]);  // [32][QS_LD]
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = threadIdx.x + 256 * u;
+  for (int u = 0; u < QP; ++u) {
+    const int e = threadIdx.x + NT * u;
     *reinterpret_cast<u32x4*>(&qs[(e >> 4) * QS_LD + 8 * (e & 15)]) = qg[u];
   }
   __syncthreads();
@@ -226,62 +235,98 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
     } while (n < nsub);
   }
 
-  // ---- merge the 4 waves (fixed order)
+  // ---- merge the NW waves (fixed order)
   if (j == 0) {
 #pragma unroll
     for (int qq = 0; qq < 2; ++qq) { red_m[w][16 * qq + li] = m_run[qq]; red_l[w][16 * qq + li] = l_run[qq]; }
   }
-  __syncthreads();
+  __syncthreads();  // also: every wave is done reading the Q tile staged in osum
   // this wave's O scaled to the workgroup maximum: lane holds query 16 qq + li,
   // dims 16 dt + 4j + r
+  float f[2];
 #pragma unroll
   for (int qq = 0; qq < 2; ++qq) {
     const int qi = 16 * qq + li;
     float M = red_m[0][qi];
 #pragma unroll
-    for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i][qi]);
-    const float f = (m_run[qq] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qq] - M);
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, red_m[i][qi]);
+    f[qq] = (m_run[qq] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run[qq] - M);
+  }
+  // eight waves: the upper half hands its O to the lower half (wave w + 4 to wave w),
+  // which then publishes the pair's sum; four waves publish their own O directly
+  if (w >= NW - NH) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      float4 val = make_float4(oacc[qq][dt][0] * f, oacc[qq][dt][1] * f, oacc[qq][dt][2] * f,
-                               oacc[qq][dt][3] * f);
-      *reinterpret_cast<float4*>(&osum[w][qi][16 * dt + 4 * j]) = val;
-    }
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<float4*>(&osum[w - (NW - NH)][16 * qq + li][16 * dt + 4 * j]) =
+            make_float4(oacc[qq][dt][0] * f[qq], oacc[qq][dt][1] * f[qq],
+                        oacc[qq][dt][2] * f[qq], oacc[qq][dt][3] * f[qq]);
+  }
+  if constexpr (NW == 8) __syncthreads();
+  if (NW == 8 && w < NH) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        float* sp = &osum[w][16 * qq + li][16 * dt + 4 * j];
+        const float4 u = *reinterpret_cast<const float4*>(sp);
+        *reinterpret_cast<float4*>(sp) =
+            make_float4(oacc[qq][dt][0] * f[qq] + u.x, oacc[qq][dt][1] * f[qq] + u.y,
+                        oacc[qq][dt][2] * f[qq] + u.z, oacc[qq][dt][3] * f[qq] + u.w);
+      }
   }
   __syncthreads();
-  // thread -> (query qi, dims 4 d4 .. +4) for 4 (query, d4) pairs; waves summed in order
+  // thread -> (query qi, dims 4 d4 .. +4) for 1024 / NT (query, d4) pairs; the NH wave
+  // pair sums added in order
   const int64_t grp = ((int64_t)b * Hq + hq) * nqt + qt;
+  constexpr int PAIRS = 1024 / NT;
+  float4 acc[PAIRS];
+  float Mq[PAIRS], Lq[PAIRS];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int e = threadIdx.x + 256 * it;
+  for (int it = 0; it < PAIRS; ++it) {
+    const int e = threadIdx.x + NT * it;
     const int qi = e >> 5, d4 = (e & 31) * 4;
-    float4 acc = *reinterpret_cast<const float4*>(&osum[0][qi][d4]);
+    acc[it] = *reinterpret_cast<const float4*>(&osum[0][qi][d4]);
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
+    for (int ww = 1; ww < NH; ++ww) {
       const float4 u = *reinterpret_cast<const float4*>(&osum[ww][qi][d4]);
-      acc.x += u.x; acc.y += u.y; acc.z += u.z; acc.w += u.w;
+      acc[it].x += u.x; acc[it].y += u.y; acc[it].z += u.z; acc[it].w += u.w;
     }
     float M = red_m[0][qi];
-    for (int i = 1; i < 4; ++i) M = fmaxf(M, red_m[i][qi]);
+    for (int i = 1; i < NW; ++i) M = fmaxf(M, red_m[i][qi]);
     float L = 0.f;
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NW; ++i)
       L += (red_m[i][qi] == -INFINITY) ? 0.f : red_l[i][qi] * __builtin_amdgcn_exp2f(red_m[i][qi] - M);
-    if (nchunk == 1) {
-      const int row = qt * 32 + qi;
-      if (row < R) {
-        const float inv = 1.0f / L;
-        u16x4 r;
-        r[0] = f2bf(acc.x * inv); r[1] = f2bf(acc.y * inv); r[2] = f2bf(acc.z * inv); r[3] = f2bf(acc.w * inv);
-        *reinterpret_cast<u16x4*>(o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD + d4) = r;
-      }
-    } else {
-      float* po = part_o + (grp * nchunk + chunk) * (32 * HD);
-      *reinterpret_cast<float4*>(po + qi * HD + d4) = acc;
-      if (d4 == 0) {
-        float* pml = part_ml + (grp * nchunk + chunk) * 64;
-        pml[qi] = M;
-        pml[32 + qi] = L;
-      }
+    Mq[it] = M;
+    Lq[it] = L;
+  }
+  auto store_o = [&](int qi, int d4, float4 a, float L) {
+    const int row = qt * 32 + qi;
+    if (row < R) {
+      const float inv = 1.0f / L;
+      u16x4 r;
+      r[0] = f2bf(a.x * inv); r[1] = f2bf(a.y * inv); r[2] = f2bf(a.z * inv); r[3] = f2bf(a.w * inv);
+      *reinterpret_cast<u16x4*>(o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD + d4) = r;
+    }
+  };
+  if (nchunk == 1) {
+#pragma unroll
+    for (int it = 0; it < PAIRS; ++it) {
+      const int e = threadIdx.x + NT * it;
+      store_o(e >> 5, (e & 31) * 4, acc[it], Lq[it]);
+    }
+    return;
+  }
+  float* pc = part + (grp * nchunk + chunk) * kPartStride;
+#pragma unroll
+  for (int it = 0; it < PAIRS; ++it) {
+    const int e = threadIdx.x + NT * it;
+    const int qi = e >> 5, d4 = (e & 31) * 4;
+    *reinterpret_cast<float4*>(pc + qi * HD + d4) = acc[it];
+    if (d4 == 0) {
+      pc[32 * HD + qi] = Mq[it];
+      pc[32 * HD + 32 + qi] = Lq[it];
     }
   }
 }
@@ -291,10 +336,8 @@ __global__ __launch_bounds__(256, ONE ? 2 : 1) void attn_splitkv_bf16(
 // the 32-row tile, thread -> (row, 4 dims).  Every thread computes its row's weights
 // itself (the (m, l) pairs are 2 * nchunk broadcast loads), and the partial loads of up
 // to 16 chunks are issued together.
-constexpr int kMaxChunks = 64;
 constexpr int kCombRows = 4;
-__global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ part_o,
-                                                    const float* __restrict__ part_ml,
+__global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ part,
                                                     uint16_t* __restrict__ o, int Hq, int R,
                                                     int nqt, int nchunk) {
   const int64_t grp = blockIdx.x;
@@ -303,8 +346,7 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
   const int b = (int)(grp / ((int64_t)nqt * Hq));
   const int qi = blockIdx.y * kCombRows + (threadIdx.x >> 5), d4 = (threadIdx.x & 31) * 4;
   const int row = qt * 32 + qi;
-  const float* pml = part_ml + grp * nchunk * 64;
-  const float* pb = part_o + grp * nchunk * (32 * HD) + qi * HD + d4;
+  const float* pg = part + grp * nchunk * kPartStride;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float M = -INFINITY, L = 0.f;
   for (int c0 = 0; c0 < nchunk; c0 += 16) {
@@ -313,9 +355,10 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       const int c = min(c0 + u, nchunk - 1);  // clamped; chunks past nchunk are dropped
-      mc[u] = pml[c * 64 + qi];
-      lc[u] = pml[c * 64 + 32 + qi];
-      v[u] = *reinterpret_cast<const float4*>(pb + (int64_t)c * 32 * HD);
+      const float* pc = pg + (int64_t)c * kPartStride;
+      mc[u] = pc[32 * HD + qi];
+      lc[u] = pc[32 * HD + 32 + qi];
+      v[u] = *reinterpret_cast<const float4*>(pc + qi * HD + d4);
     }
     // online merge in chunk order (the same result as rescaling by the global max)
 #pragma unroll
@@ -540,32 +583,35 @@ __global__ __launch_bounds__(128) void attn_f32(const float* __restrict__ q,
   }
 }
 
+constexpr int kMaxChunks = 64;
+
+// Step attention (at most 64 query rows), 32-key sub-tiles per wave:
+//  * one sub-tile per wave in eight-wave workgroups (256-key chunks: half the partials
+//    to merge of four-wave chunks) when that gives 256 to 1024 workgroups;
+//  * else one sub-tile per wave in four-wave workgroups if that needs at most 512;
+//  * else four waves walking several sub-tiles each (a register-heavy kernel, one
+//    workgroup per CU), with chunks sized for about 256 workgroups.
 AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
   AttnPlan p;
   if (dtype == F32) { p.kind = 0; return p; }
   if (R <= 64) {
     p.kind = 1;
     p.nqt = (R + 31) / 32;
-    const int base = B * Hq * p.nqt;
-    if ((int64_t)base * ((S + 127) / 128) <= 512 && (S + 127) / 128 <= kMaxChunks) {
-      // one 32-key sub-tile per wave, up to two workgroups per CU
-      p.nchunk = (S + 127) / 128;
-      p.nsub = 1;
-      if (p.nchunk > 1) p.part_floats = (size_t)base * p.nchunk * (32 * HD + 64);
-      return p;
+    const int64_t base = (int64_t)B * Hq * p.nqt;
+    const int n8 = (S + 255) / 256, n4 = (S + 127) / 128;
+    if (base * n8 >= 256 && base * n8 <= 1024 && n8 <= kMaxChunks) {
+      p.nw = 8; p.nsub = 1; p.nchunk = n8;
+    } else if (base * n4 <= 512 && n4 <= kMaxChunks) {
+      p.nw = 4; p.nsub = 1; p.nchunk = n4;
+    } else {
+      int64_t target = (256 + base - 1) / base;      // chunks wanted for ~256 workgroups
+      if (target < 1) target = 1;
+      int ck = (int)((S + target - 1) / target);     // keys per chunk
+      ck = (ck + 127) / 128 * 128;                   // 4 waves x 32-key sub-tiles
+      if ((S + ck - 1) / ck > kMaxChunks) ck = ((S + kMaxChunks - 1) / kMaxChunks + 127) / 128 * 128;
+      p.nw = 4; p.nsub = ck / 128; p.nchunk = (S + ck - 1) / ck;
     }
-    int target = (256 + base - 1) / base;          // chunks wanted for ~256 workgroups
-    if (target < 1) target = 1;
-    int ck = (S + target - 1) / target;             // keys per chunk
-    ck = (ck + 127) / 128 * 128;                    // 4 waves x 32-key sub-tiles
-    int nchunk = (S + ck - 1) / ck;
-    if (nchunk > kMaxChunks) {
-      ck = ((S + kMaxChunks - 1) / kMaxChunks + 127) / 128 * 128;
-      nchunk = (S + ck - 1) / ck;
-    }
-    p.nchunk = nchunk;
-    p.nsub = ck / 128;
-    if (p.nchunk > 1) p.part_floats = (size_t)base * p.nchunk * (32 * HD + 64);
+    if (p.nchunk > 1) p.part_floats = (size_t)base * p.nchunk * kPartStride;
   } else {
     p.kind = 2;
     p.nqt = (R + 127) / 128;
@@ -587,23 +633,22 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
   }
   const float scale_log2 = kLog2e / sqrtf((float)D);
   if (p.kind == 1) {
-    const int64_t groups = (int64_t)B * Hq * p.nqt;
-    float* part_o = part;
-    float* part_ml = part ? part + groups * p.nchunk * (32 * HD) : nullptr;
+    if (p.nchunk > 1 && !part) return hipErrorInvalidValue;
     const dim3 grid(p.nchunk, Hq * p.nqt, B);
-    if (p.nsub == 1)
-      attn_splitkv_bf16<true><<<grid, 256, 0, st>>>(
-          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
-          S, Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part_o, part_ml);
-    else
-      attn_splitkv_bf16<false><<<grid, 256, 0, st>>>(
-          (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
-          S, Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part_o, part_ml);
+#define DLLM_ATTN(NWV, ONEV)                                                                  \
+  attn_splitkv_bf16<NWV, ONEV><<<grid, NWV * 64, 0, st>>>(                                    \
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, S, \
+      Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part)
+    if (p.nw == 8 && p.nsub == 1) DLLM_ATTN(8, true);
+    else if (p.nw == 4 && p.nsub == 1) DLLM_ATTN(4, true);
+    else if (p.nw == 4) DLLM_ATTN(4, false);
+    else return hipErrorInvalidValue;  // the plan never asks for 8 waves x several sub-tiles
+#undef DLLM_ATTN
     if (p.nchunk > 1) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      attn_combine<<<dim3((unsigned)groups, 32 / kCombRows), 32 * kCombRows, 0, st>>>(
-          part_o, part_ml, (uint16_t*)o, Hq, R, p.nqt, p.nchunk);
+      attn_combine<<<dim3((unsigned)(B * Hq * p.nqt), 32 / kCombRows), 32 * kCombRows, 0, st>>>(
+          part, (uint16_t*)o, Hq, R, p.nqt, p.nchunk);
     }
   } else {
     attn_flash_bf16<<<dim3(p.nqt, Hq, B), 256, 0, st>>>(

@@ -151,6 +151,7 @@ hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e,
 struct AttnPlan {
   int kind = 0;          // 0: fp32 simple, 1: bf16 split-KV (R <= 64), 2: bf16 flash
   int nqt = 0, nchunk = 0, nsub = 0;
+  int nw = 4;            // split-KV: waves per workgroup (4 or 8)
   size_t part_floats = 0;
   int counters = 0;      // unused: chunk partials are merged by a second kernel
 };

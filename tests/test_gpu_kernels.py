@@ -181,14 +181,21 @@ def run_attn(lib, q, k, v, B, Hq, Hkv, R, S, D, dtype):
 
 ATTN_CASES = [
     # name, B, Hq, Hkv, R, S, dtype
+    # (plan: four-wave chunks of 128 keys, 8 chunks)
     ("llada_block32_kv1024", 1, 32, 32, 32, 1024, "bf16"),
+    # eight-wave chunks of 256 keys, ragged last chunk (the 8B step shape)
     ("llada_block32_kv2024", 1, 32, 32, 32, 2024, "bf16"),
+    # eight-wave chunks whose last chunk has seven waves past the last key
+    ("nw8_masked_waves", 1, 32, 32, 32, 1800, "bf16"),
     ("gqa_7to1_b2", 2, 28, 4, 32, 1000, "bf16"),
-    ("gqa_7to1_b8_multi_subtile", 8, 28, 4, 32, 1024, "bf16"),
-    # several sub-tiles per wave with an odd count (3 and 5) and a ragged last chunk
-    # (chunks of 384 and 640 keys)
-    ("multi_subtile_odd_ragged", 2, 32, 32, 32, 1500, "bf16"),
-    ("multi_subtile_long_ragged", 1, 32, 32, 32, 4100, "bf16"),
+    # the 7B batch-8 step shape (eight-wave chunks, 896 workgroups)
+    ("gqa_7to1_b8", 8, 28, 4, 32, 1024, "bf16"),
+    # several sub-tiles per wave: 10 per wave over 2 chunks (GQA), 9 (odd) per wave over
+    # 4 chunks with a ragged last one
+    ("gqa_7to1_b8_multi_subtile", 8, 28, 4, 32, 2500, "bf16"),
+    ("multi_subtile_odd_ragged", 2, 32, 32, 32, 4400, "bf16"),
+    # 17 eight-wave chunks: the merge walks its chunks in three rounds of loads
+    ("many_chunks_ragged", 1, 32, 32, 32, 4100, "bf16"),
     ("ragged_rows_keys", 1, 4, 2, 20, 77, "bf16"),
     ("two_row_tiles", 1, 2, 1, 64, 300, "bf16"),
     ("flash_many_rows", 1, 2, 2, 200, 333, "bf16"),
