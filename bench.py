@@ -54,12 +54,14 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def logit_scale(name: str) -> float:
+def logit_scale(wl) -> float:
+    """The oracle-calibrated logit scale of a named random-init 8B/7B workload
+    (tests/golden/logit_scales.json), else the scale its config gives."""
     p = os.path.join(ROOT, "tests", "golden", "logit_scales.json")
-    if name == "tiny_dual":
-        return synth.WORKLOADS[name].model.logit_scale
-    tab = json.load(open(p))
-    return float(tab[name]["logit_scale"])
+    tab = json.load(open(p)) if os.path.exists(p) else {}
+    if wl.name in tab:
+        return float(tab[wl.name]["logit_scale"])
+    return wl.model.logit_scale
 
 
 def kernel_work(cls: str, wl, R_step: int):
@@ -419,7 +421,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", default="llada8b_dual_p1000_g1024")
+    ap.add_argument("--workload", default="llada8b_dual_p1000_g1024",
+                    help=f"a named workload: {', '.join(sorted(synth.WORKLOADS))}")
+    ap.add_argument("--config", default=None,
+                    help="a workload JSON file (the format of synth/workloads/*.json) instead "
+                         "of a named workload")
     ap.add_argument("--gen-len", type=int, default=0, help="override (for quick runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernels", action="store_true", help="skip the kernel-only rates")
@@ -470,8 +476,8 @@ def main():
     if a.kernels_only:
         print(json.dumps({"kernels": kernel_only(lib, torch, bd)}), flush=True)
         return
-    wl = synth.with_scale(synth.WORKLOADS[a.workload],
-                          a.logit_scale if a.logit_scale else logit_scale(a.workload))
+    base = synth.load_workload(a.config) if a.config else synth.WORKLOADS[a.workload]
+    wl = synth.with_scale(base, a.logit_scale if a.logit_scale else logit_scale(base))
     if a.gen_len:
         wl = replace(wl, gen_len=a.gen_len)
     log(f"workload {wl.name}: B={wl.batch} P={wl.prompt_len} G={wl.gen_len} K={wl.block_len} "

@@ -84,11 +84,22 @@ class Model:
         return Model(lib, m, t)
 
 
+# Debug runs: bytes of guard band on each side of the KV cache and the workspace, and the
+# 32-bit canary they hold.  The buffers themselves start filled with 0xFF bytes, a NaN in
+# both fp32 and bf16, so that any read of a byte the library has not written first shows
+# up as NaN in the results.
+GUARD_BYTES = 1 << 16
+CANARY = 0x5CA1AB1E
+
+
 class Session:
-    """Tokens, KV cache and workspace of one batch of sequences."""
+    """Tokens, KV cache and workspace of one batch of sequences.
+
+    With ``debug`` the KV cache and the workspace are NaN-poisoned before first use and
+    framed by canary guard bands; ``check_guards()`` raises if a call wrote outside them."""
 
     def __init__(self, model: Model, prompt, gen_len: int, block_len: int, threshold: float,
-                 mode: str, device="cuda"):
+                 mode: str, device="cuda", debug: bool = False):
         torch = _torch()
         self.model, self.lib = model, model.lib
         prompt = torch.as_tensor(np.asarray(prompt), dtype=torch.int32)
@@ -112,14 +123,46 @@ class Session:
         if cb == 0 or wb == 0:
             # report why through a call that validates
             self.lib.check(self.lib.raw("dllm_prefill_cache")(mp, sp, None), "Session")
-        self.cache = torch.empty(cb, dtype=torch.uint8, device=device)
-        self.ws = torch.empty(wb, dtype=torch.uint8, device=device)
+        self.debug = debug
+        if debug:
+            self._guarded = {}
+            self.cache = self._guarded_buffer("kv_cache", cb, device)
+            self.ws = self._guarded_buffer("workspace", wb, device)
+        else:
+            self.cache = torch.empty(cb, dtype=torch.uint8, device=device)
+            self.ws = torch.empty(wb, dtype=torch.uint8, device=device)
         self.desc.kv_cache = self.cache.data_ptr()
         self.desc.kv_cache_bytes = cb
         self.desc.workspace = self.ws.data_ptr()
         self.desc.workspace_bytes = wb
         self.n_unmasked = torch.zeros(B, dtype=torch.int32, device=device)
         self.remaining = torch.zeros(B, dtype=torch.int32, device=device)
+
+    def _guarded_buffer(self, name: str, nbytes: int, device):
+        """A NaN-poisoned buffer of nbytes inside a larger allocation whose first and last
+        GUARD_BYTES hold the canary; returns the view of the inner bytes."""
+        torch = _torch()
+        g = GUARD_BYTES // 4
+        n4 = (nbytes + 3) // 4
+        full = torch.full((2 * g + n4,), CANARY, dtype=torch.int32, device=device)
+        full[g:g + n4] = -1                       # 0xFFFFFFFF: NaN as fp32 and as two bf16
+        self._guarded[name] = (full, g, n4)
+        return full.view(torch.uint8)[4 * g:4 * g + nbytes]
+
+    def check_guards(self):
+        """Raise if any byte of a guard band around the cache or the workspace changed."""
+        if not self.debug:
+            return
+        torch = _torch()
+        torch.cuda.synchronize(self.tokens.device)
+        want = np.int32(CANARY)
+        for name, (full, g, n4) in self._guarded.items():
+            for side, band in (("before", full[:g]), ("after", full[g + n4:])):
+                h = band.cpu().numpy()
+                bad = np.nonzero(h != want)[0]
+                if bad.size:
+                    raise RuntimeError(f"{name}: guard band {side} the buffer overwritten at "
+                                       f"{bad.size} words (first at word {int(bad[0])})")
 
     def _args(self):
         return C.byref(self.model.desc), C.byref(self.desc)

@@ -270,29 +270,42 @@ def make_prompt(wl: Workload) -> np.ndarray:
 # Named workloads
 # ---------------------------------------------------------------------------------
 
-TINY = ModelShape(n_layers=2, d_model=64, n_heads=4, n_kv_heads=4, head_dim=16, d_ffn=256,
-                  vocab=256, logit_scale=8.0, dtype="f32")
-LLADA_8B = ModelShape(n_layers=32, d_model=4096, n_heads=32, n_kv_heads=32, head_dim=128,
-                      d_ffn=12288, vocab=126464, dtype="bf16")
-DREAM_7B = ModelShape(n_layers=28, d_model=3584, n_heads=28, n_kv_heads=4, head_dim=128,
-                      d_ffn=18944, vocab=152064, dtype="bf16")
+# Named workloads, one JSON file each in synth/workloads/ (shapes, batch, lengths, block,
+# cache mode, threshold, seeds).  The logit scales of the random-init 8B/7B shapes are not
+# in them: they are calibrated by the oracle (tests/golden/make_logit_scales.py) so that
+# about 30 % of the masked positions of the first step reach confidence 0.9.
+WORKLOAD_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "workloads")
 
-# Logit scales for the random-init 8B/7B shapes: chosen (by oracle.calibrate on one
-# prefill forward) so that about 30 % of the masked positions reach confidence 0.9.
-# Filled in from tests/golden/logit_scales.json when present.
-WORKLOADS = {
-    "tiny_dual": Workload("tiny_dual", TINY, batch=1, prompt_len=16, gen_len=32, block_len=8,
-                          cache_mode="dual"),
-    "llada8b_prefix_p256_g256": Workload("llada8b_prefix_p256_g256", LLADA_8B, batch=1,
-                                         prompt_len=256, gen_len=256, block_len=32,
-                                         cache_mode="prefix"),
-    "llada8b_dual_p1000_g1024": Workload("llada8b_dual_p1000_g1024", LLADA_8B, batch=1,
-                                         prompt_len=1000, gen_len=1024, block_len=32,
-                                         cache_mode="dual"),
-    "dream7b_dual_b8_p512_g512": Workload("dream7b_dual_b8_p512_g512", DREAM_7B, batch=8,
-                                          prompt_len=512, gen_len=512, block_len=32,
-                                          cache_mode="dual"),
-}
+
+def workload_from_dict(d: dict) -> Workload:
+    """A Workload from its JSON form (the keys of Workload, with "model" the keys of
+    ModelShape); unknown keys are rejected so that a typo cannot pass silently."""
+    d = dict(d)
+    d.pop("description", None)
+    m = dict(d.pop("model"))
+    mk = set(ModelShape.__dataclass_fields__)
+    wk = set(Workload.__dataclass_fields__) - {"model"}
+    if set(m) - mk or set(d) - wk:
+        raise ValueError(f"unknown workload keys: {sorted((set(m) - mk) | (set(d) - wk))}")
+    return Workload(model=ModelShape(**m), **d)
+
+
+def load_workload(path: str) -> Workload:
+    import json
+    with open(path) as f:
+        return workload_from_dict(json.load(f))
+
+
+def _load_named() -> dict:
+    out = {}
+    for fn in sorted(os.listdir(WORKLOAD_DIR)):
+        if fn.endswith(".json"):
+            wl = load_workload(os.path.join(WORKLOAD_DIR, fn))
+            out[wl.name] = wl
+    return out
+
+
+WORKLOADS = _load_named()
 
 
 def with_scale(wl: Workload, scale: float) -> Workload:

@@ -39,3 +39,32 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monk
     with open(csrc / b.COUNTED_SOURCES[0], "a") as fh:   # a kernel source changes
         fh.write("\n// changed\n")
     assert b.counters_for("CLS", "wl") is None
+
+
+def test_generation_roofline_arithmetic():
+    """The whole-generation roofline from the NFE: at the 8B DualCache shape a refresh is
+    2 B S (layer params) L + 4 B S^2 Hq D L = 30.4 TFLOP (12.2 ms at 2.5 PFLOP/s) and a cached
+    step streams the 15.0 GB of weights plus the 1.06 GB KV cache (2.0 ms at 8 TB/s)."""
+    import synth
+    b = load_bench()
+    wl = synth.WORKLOADS["llada8b_dual_p1000_g1024"]
+    r = b.generation_roofline(wl, 32, 918, 4.84)
+    assert abs(r["refresh_tflop"] - 30.4) < 0.05
+    assert abs(r["refresh_roof_ms"] - 12.16) < 0.01
+    assert abs(r["step_gb"] - 16.056) < 0.001
+    assert r["n_cached_steps"] == 886
+    # 32 (refresh + fused-step tail) + 886 cached steps
+    tail = (b.layer_params(wl.model) + wl.model.vocab * wl.model.d_model) * 2 / 8e12
+    want = 32 * (12.16e-3 + tail) + 886 * 2.007e-3
+    assert abs(r["t_roof_s"] - want) < 2e-3
+    assert abs(r["frac"] - r["t_roof_s"] / 4.84) < 1e-3
+
+
+def test_bench_accepts_a_workload_file(tmp_path):
+    b = load_bench()
+    import synth
+    wl = synth.load_workload(os.path.join(synth.WORKLOAD_DIR, "llada8b_dual_p1000_g1024.json"))
+    # the named 8B workloads take their oracle-calibrated scale, a custom one its own
+    assert abs(b.logit_scale(wl) - 7.3032) < 1e-3
+    from dataclasses import replace
+    assert b.logit_scale(replace(wl, name="custom")) == wl.model.logit_scale

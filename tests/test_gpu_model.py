@@ -520,3 +520,35 @@ def test_cache_staleness_matches_oracle(lib, kind, mode):
         while not osess.block_done(b):
             osess.step(b)
     print(f"worst staleness difference {worst:.2e}")
+
+
+@pytest.mark.parametrize("kind,mode", [("fp32", "dual"), ("bf16", "dual"), ("bf16", "prefix")])
+def test_debug_mode_poisoned_buffers_and_guard_bands(lib, kind, mode):
+    """Debug sessions start with a NaN-poisoned KV cache and workspace framed by canary
+    guard bands.  A whole generation gives the same tokens as a normal session (no kernel
+    reads a byte it has not written first), every guard band is intact afterwards, the
+    cache padding past the last position is still the poison (never written), and a
+    guard band that is overwritten is reported."""
+    if kind == "fp32":
+        wl = replace(synth.WORKLOADS["tiny_dual"], cache_mode=mode)
+    else:
+        wl = small_bf16(Hq=2, Hkv=1, mode=mode, B=2, K=16, P=40)
+    model = gpu_model(lib, wl)
+    prompt = synth.make_prompt(wl)
+    want, st_w = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, mode).generate()
+    s = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, mode, debug=True)
+    got, st_g = s.generate()
+    s.check_guards()
+    assert np.array_equal(got, want) and st_g["steps_per_block"] == st_w["steps_per_block"]
+    # layer 0 K of sequence 0, KV head 0: positions [S, Sp) were never written
+    m = wl.model
+    esz = 4 if m.dtype == "f32" else 2
+    S, Sp = wl.seq_len, (wl.seq_len + 63) // 64 * 64
+    k0 = s.cache[: Sp * m.head_dim * esz].cpu().numpy().view(np.uint8)
+    pad = k0[S * m.head_dim * esz:]
+    assert pad.size > 0 and np.all(pad == 0xFF)
+    # a write into a guard band is caught
+    full, g, n4 = s._guarded["workspace"]
+    full[g + n4 + 5] = 0
+    with pytest.raises(RuntimeError, match="workspace: guard band after"):
+        s.check_guards()

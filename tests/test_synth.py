@@ -77,3 +77,40 @@ def test_weight_shapes_and_scale():
     assert np.all(W["attn_norm.0"] == 1.0)
     s = W["w_down.0"].std() * np.sqrt(m.d_ffn)
     assert 0.9 < s < 1.1
+
+
+def test_named_workloads_have_the_stated_shapes():
+    """The workload files hold the shapes and settings the workloads are defined by: a tiny
+    fp32 parity model, the LLaDA-8B shape in prefix and DualCache settings, and the
+    Dream-7B shape with grouped-query attention and a batch of 8."""
+    W = synth.WORKLOADS
+    t = W["tiny_dual"]
+    assert (t.model.n_layers, t.model.d_model, t.model.n_heads, t.model.head_dim, t.model.d_ffn,
+            t.model.vocab, t.model.mask_id, t.model.logit_scale, t.model.dtype) == \
+        (2, 64, 4, 16, 256, 256, 255, 8.0, "f32")
+    assert (t.batch, t.prompt_len, t.gen_len, t.block_len, t.cache_mode, t.threshold) == \
+        (1, 16, 32, 8, "dual", 0.9)
+    for name, mode, P, G in (("llada8b_prefix_p256_g256", "prefix", 256, 256),
+                             ("llada8b_dual_p1000_g1024", "dual", 1000, 1024)):
+        w = W[name]
+        assert (w.model.n_layers, w.model.d_model, w.model.n_heads, w.model.n_kv_heads,
+                w.model.head_dim, w.model.d_ffn, w.model.vocab, w.model.dtype) == \
+            (32, 4096, 32, 32, 128, 12288, 126464, "bf16")
+        assert (w.batch, w.prompt_len, w.gen_len, w.block_len, w.cache_mode) == (1, P, G, 32, mode)
+    d = W["dream7b_dual_b8_p512_g512"]
+    assert (d.model.n_layers, d.model.d_model, d.model.n_heads, d.model.n_kv_heads,
+            d.model.head_dim, d.model.d_ffn, d.model.vocab) == (28, 3584, 28, 4, 128, 18944, 152064)
+    assert (d.batch, d.prompt_len, d.gen_len, d.block_len, d.cache_mode) == (8, 512, 512, 32, "dual")
+
+
+def test_workload_files_round_trip_and_reject_unknown_keys(tmp_path):
+    import json
+    import pytest
+    src = json.load(open(f"{synth.WORKLOAD_DIR}/tiny_dual.json"))
+    p = tmp_path / "w.json"
+    p.write_text(json.dumps(src))
+    assert synth.load_workload(str(p)) == synth.WORKLOADS["tiny_dual"]
+    bad = dict(src, treshold=0.5)
+    p.write_text(json.dumps(bad))
+    with pytest.raises(ValueError):
+        synth.load_workload(str(p))
