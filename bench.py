@@ -163,13 +163,14 @@ def host_cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int, repeats: int = 3):
+def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int, budget_s: float = 12.0):
     """The oracle as it stands, in float32 with bf16 rounding at its storage points (its
     timed mode for bf16 models), on a bounded sample of the workload: one full layer over
     all S rows (a refresh layer) and one cached-step layer over the block rows against the
-    cache, plus the LM head and the confidence/unmask rule, each run ``repeats`` times
-    (the fastest kept).  Scaled by the layer count and combined with the GPU run's NFE
-    into generated tokens/s (extrapolated)."""
+    cache, plus the LM head and the confidence/unmask rule, each run three times or more,
+    until about ``budget_s`` seconds of work are spent (the fastest run of each kept).
+    Scaled by the layer count and combined with the GPU run's NFE into generated tokens/s
+    (extrapolated)."""
     from threadpoolctl import threadpool_info
     from oracle import decode
     from oracle import model as om
@@ -185,10 +186,11 @@ def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int, repeats: int = 3):
     B, P, S, K = wl.batch, wl.prompt_len, wl.seq_len, wl.block_len
     tokens = np.concatenate([prompt, np.full((B, wl.gen_len), m.mask_id, np.int64)], axis=1)
 
-    def best(f):
+    # the four parts get shares of the budget: refresh layer 3/4, the rest 1/12 each
+    def best(f, share):
         ts = []
         out = None
-        for _ in range(repeats):
+        while len(ts) < 3 or (sum(ts) < share * budget_s and len(ts) < 20):
             t0 = time.perf_counter()
             out = f()
             ts.append(time.perf_counter() - t0)
@@ -199,21 +201,22 @@ def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int, repeats: int = 3):
         q, k, v = om.layer_qkv(M, 0, x, np.arange(S))
         om.layer_rest(M, 0, x, q, k, v)
         return k, v
-    t_ref_layer, spent, (k, v) = best(ref_layer)
+    t_ref_layer, spent, (k, v) = best(ref_layer, 0.75)
     cache = om.KVCache(1, B, m.n_kv_heads, S, m.head_dim, dt)
     cache.K[0][...] = k
     cache.V[0][...] = v
-    t_step_1, sp, logits = best(lambda: om.cached_step(M, tokens, cache, P, P + K, wl.cache_mode))
+    t_step_1, sp, logits = best(lambda: om.cached_step(M, tokens, cache, P, P + K, wl.cache_mode),
+                                1 / 12)
     spent += sp
 
     def dec():
         conf, arg = decode.confidence_argmax(logits.reshape(B * K, -1), m.mask_id)
         decode.unmask(tokens[:, P:P + K], conf.reshape(B, K), arg.reshape(B, K), m.mask_id,
                       wl.threshold)
-    t_dec, sp, _ = best(dec)
+    t_dec, sp, _ = best(dec, 1 / 12)
     spent += sp
     # a 1-layer cached step = 1 layer + LM head; split the LM head off with a timed call
-    t_head, sp, _ = best(lambda: om.lm_head(M, np.zeros((B, K, m.d_model), dt)))
+    t_head, sp, _ = best(lambda: om.lm_head(M, np.zeros((B, K, m.d_model), dt)), 1 / 12)
     spent += sp
     t_step_layer = max(t_step_1 - t_head, 0.0)
     L = m.n_layers
@@ -226,7 +229,8 @@ def cpu_baseline(wl, nfe_steps: int, nfe_refreshes: int, repeats: int = 3):
     return {
         "value": round(B * wl.gen_len / total, 4), "unit": "tokens/s", "cores": threads,
         "kind": "oracle",
-        "sample": (f"oracle in {prec}, 1 of {L} layers timed (best of {repeats}): "
+        "sample": (f"oracle in {prec}, 1 of {L} layers timed (best of at least 3 runs, "
+                   f"{spent:.1f} s of work): "
                    f"full-sequence layer {t_ref_layer:.2f} s, cached-step layer "
                    f"{t_step_layer:.3f} s, LM head {t_head:.3f} s, decode {t_dec:.3f} s; "
                    f"scaled x{L} and by the GPU run's NFE ({nfe_steps} steps, "

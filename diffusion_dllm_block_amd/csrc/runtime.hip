@@ -887,11 +887,11 @@ dllm_status dllm_kernel_confidence_unmask_noalloc(const void* logits, int32_t lo
   char* base = nullptr;
   dllm_status s = scratch_for(st, &base);
   if (s) return s;
-  // every (row, slice) triple is written by pass 1 before pass 2 reads it: nothing to clear
+  // every (row, slice) triple is written by pass 1 before pass 2 reads it: nothing to clear.
+  // No kernel-class timing here: its events would be created on demand.
   float* pm = (float*)base;
   float* ps_ = pm + kScratchParts;
   int* pi = (int*)(pm + 2 * kScratchParts);
-  ProfScope ps(DLLM_K_CONF_UNMASK, st);
   HIP_TRY(launch_conf_unmask(logits_dtype, p, logits, B, K, V, mask_id, tau, tokens_block,
                              ld_tokens, conf, argmax, n_unmasked, remaining, unmasked_idx, pm, ps_,
                              pi, st));
