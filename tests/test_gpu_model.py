@@ -552,3 +552,47 @@ def test_debug_mode_poisoned_buffers_and_guard_bands(lib, kind, mode):
     full[g + n4 + 5] = 0
     with pytest.raises(RuntimeError, match="workspace: guard band after"):
         s.check_guards()
+
+
+def test_prefix_mode_empty_prompt_every_step_equals_full_forward(lib):
+    """With an empty prompt, a prefix-mode step of block 0 recomputes every position, so
+    each of its cached steps (not only the first after the prefill) must give the no-cache
+    full forward's logits (ccyt168.com Fast-dLLM article, section 1.1: the prefix cache
+    keeps only what precedes the block).  fp32 model at 1e-4, teacher-forced along the
+    oracle's trajectory, one token per step (tau > 1) so the block takes 8 steps."""
+    wl = replace(synth.WORKLOADS["tiny_dual"], prompt_len=0, gen_len=24, cache_mode="prefix",
+                 threshold=1.5)
+    m = wl.model
+    M = om.OracleModel(wl)
+    prompt = np.zeros((wl.batch, 0), dtype=np.int64)
+    osess = OSession(M, prompt, wl.gen_len, wl.block_len, wl.threshold, "prefix")
+    gsess = Session(gpu_model(lib, wl), prompt, wl.gen_len, wl.block_len, wl.threshold, "prefix")
+    osess.refresh()
+    gsess.prefill()
+    n = 0
+    while not osess.block_done(0):
+        s0, s1 = osess.block_span(0)
+        gsess.tokens.copy_(torch.from_numpy(osess.tokens.astype(np.int32)))
+        _, ref = om.full_forward(M, osess.tokens, logit_rows=slice(s0, s1))
+        g = gsess.step(0)
+        torch.cuda.synchronize()
+        got = g["logits"].cpu().numpy().reshape(ref.shape).astype(np.float64)
+        assert rel_inf(got, ref) < 1e-4, f"step {n + 1}"
+        grade_confidence_stage(got.reshape(-1, m.vocab), g["conf"].cpu().numpy(),
+                               g["argmax"].cpu().numpy(), m.mask_id)
+        osess.step(0)
+        n += 1
+    assert n == wl.block_len
+
+
+@pytest.mark.parametrize("kind", ["fp32", "bf16"])
+def test_teacher_forced_largest_block(lib, kind):
+    """Blocks of 64 positions, the largest the library takes (one wave ballot per block):
+    teacher-forced parity with every step graded per stage."""
+    if kind == "fp32":
+        wl = replace(synth.WORKLOADS["tiny_dual"], gen_len=128, block_len=64, threshold=0.7)
+        st = teacher_forced(lib, wl, 1e-4, CONF_TOL_F32)
+    else:
+        wl = small_bf16(Hq=2, Hkv=1, mode="dual", B=2, P=40, G=128, K=64)
+        st = teacher_forced(lib, wl, 2e-2)
+    assert st["steps"] >= 2
