@@ -1005,11 +1005,20 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     p.mt = (M <= 16) ? 1 : (M <= 32) ? 2 : 4;
     p.ntn = (Nv + 15) / 16;  // 16-column groups
     p.ntm = 1;
-    // per-wave K sub-range KS (the workgroup covers 8 KS): the largest of 256/128/64/32
-    // with K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 64)
+    // per-wave K sub-range KS (the workgroup covers 8 KS): among 256/128/64 with
+    // K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 64), the
+    // largest that still gives every workgroup at least 4 of the 16-column groups to walk
+    // (a workgroup with fewer spends most of its time staging its activation slice and
+    // waiting for its first weights: the 8B output projection, 2 groups per workgroup at
+    // 256, runs 10.3 us at 256 and 8.4 us at 128), else the largest (32 if none)
     int ks = 32;
+    bool found = false;
+    const int ngrp16 = (Nv + 15) / 16;
     for (int c : {256, 128, 64}) {
-      if (K % (8 * c) == 0 && (p.mt <= 2 || c <= 64)) { ks = c; break; }
+      if (K % (8 * c) != 0 || (p.mt > 2 && c > 64)) continue;
+      const int per_range = std::max(1, num_cus() / (K / (8 * c)));  // workgroups per K range
+      if (!found) { ks = c; found = true; }
+      if (ngrp16 >= 4 * per_range) { ks = c; break; }
     }
     p.kchunk = 8 * ks;
     p.splits = K / p.kchunk;
