@@ -443,15 +443,15 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
   // K stages of DK columns in a ring of NSTG LDS slots, filled by direct global->LDS
   // loads (no staging registers): each wave issues CPR/2 16-byte-per-lane loads of A
   // and of B per stage, each writing 1 KB of LDS (64 / CPR tile rows).  Rows are stored
-  // unpadded with the 16-byte chunks XOR-swizzled by row, so the MFMA operand reads
-  // (32 rows at one k offset) spread over all banks.
+  // unpadded with the 16-byte chunks XOR-swizzled by row (the mid kernel's layout note),
+  // so the MFMA operand reads (32 rows at one k offset) are free of bank conflicts.
   constexpr int CPR = DK / 8;                  // 16-byte chunks per tile row
   constexpr int RPI = 64 / CPR;                // tile rows per load instruction
   constexpr int NI = 32 / RPI;                 // load instructions per wave per matrix
   constexpr int HALF = BG_T * DK * 2;          // A (or B) bytes per stage
   constexpr int STG = 2 * HALF;
   const int nst = (ke - kb) / DK;
-  auto swz = [](int r) { return CPR == 4 ? ((r >> 1) & 3) : (r & (CPR - 1)); };
+  auto swz = [](int r) { return CPR == 4 ? ((r >> 2) & 3) : ((r >> 1) & (CPR - 1)); };
   const uint16_t* asrc[NI];
   const uint16_t* bsrc[NI];
 #pragma unroll
@@ -623,9 +623,14 @@ __global__ __launch_bounds__(MD_THREADS, 1) void gemm_mid_bf16(
   const int tid = threadIdx.x;
   const int w = tid >> 6, wm = w & 3, wn = w >> 2, l = tid & 63, lr = l & 31, g = l >> 5;
   const int Nt = Nv - ndp * MD_BN;  // row stride of the partials
-  // 16-byte chunk c of tile row r sits in slot c ^ (r & 7) of the row's 128 bytes, so
-  // the operand reads (32 rows at one k offset) spread over all banks
-  auto swz = [](int r) { return r & 7; };
+  // 16-byte chunk c of tile row r sits in slot c ^ ((r >> 1) & 7) of the row's 128 bytes.
+  // LDS serves a 16-byte-per-lane read 16 lanes per clock from 64 four-byte banks (256
+  // bytes); an operand read puts 16 consecutive rows at one k offset in those lanes.  Rows
+  // r and r + 1 already fall in different halves of the 256 bytes, so the key changes
+  // every second row and the 16 rows land in 16 distinct 16-byte slots (keyed by r & 7,
+  // rows r and r + 8 collided: half the read rate, measured).  For 64-byte rows (four
+  // per 256 bytes) the key is (r >> 2) & 3.
+  auto swz = [](int r) { return (r >> 1) & 7; };
 
   for (int u = blockIdx.x; u < nunits; u += gridDim.x) {
     const bool whole = u < ndp;
