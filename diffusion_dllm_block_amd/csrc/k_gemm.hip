@@ -23,6 +23,7 @@
 //     same split-K schemes for shapes with too few tiles.
 //   gemm_f32: SIMT fp32 kernel for fp32 models (32x128 tiles).
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -45,10 +46,11 @@ __device__ __forceinline__ uint16_t swiglu_bf16(float gt, float up) { return f2b
 
 __device__ __forceinline__ int acc_row(int v, int g) { return 8 * (v >> 2) + 4 * g + (v & 3); }
 
-// Epilogue over an fp32 tile in LDS: tile[r * ldt + c] is output row m0 + r and virtual
-// column vc0 + c (c < 128).
+// Element-by-element epilogue over an fp32 tile in LDS (tile[r * ldt + c] is output row
+// m0 + r and virtual column vc0 + c, c < 128): the fallback of epilogue() for shapes or
+// pointers that the 4-wide form does not cover.
 template <typename T, int EPI>
-__device__ void epilogue(const float* tile, int ldt, int rows, int m0, int vc0, int M, int Nv,
+__device__ void epilogue_scalar(const float* tile, int ldt, int rows, int m0, int vc0, int M, int Nv,
                          const EpiArgs& e) {
   const int tid = threadIdx.x, nt = blockDim.x;
   if constexpr (EPI == EPI_STORE || EPI == EPI_F32 || EPI == EPI_RESID) {
@@ -99,6 +101,139 @@ __device__ void epilogue(const float* tile, int ldt, int rows, int m0, int vc0, 
         T* dst = (T*)e.vtc + ((int64_t)bs * e.Hkv + h) * D * (int64_t)e.Sp;
         Elt<T>::store(dst, vt_off(j, pos, D), x1);
         Elt<T>::store(dst, vt_off(j + half, pos, D), x2);
+      }
+    }
+  }
+}
+
+// 4 adjacent outputs: 8 bytes of bf16 or 16 bytes of fp32 (callers check the alignment).
+template <typename T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<u16x4*>(p) = u16x4{f2bf(a), f2bf(b), f2bf(c), f2bf(d)};
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  }
+}
+__device__ __forceinline__ bool aligned_to(const void* p, int bytes) {
+  return ((uintptr_t)p & (uintptr_t)(bytes - 1)) == 0;
+}
+__device__ __forceinline__ int ilog2(int v) { return 31 - __builtin_clz(v); }
+
+// Epilogue over an fp32 tile in LDS: tile[r * ldt + c] is output row m0 + r and virtual
+// column vc0 + c (c < 128); ldt % 4 == 0 and the tile 16-byte aligned.  Each thread takes
+// 4 adjacent outputs (16-byte LDS reads, one 8- or 16-byte store) and works out a row's
+// sequence and position once per row; V is written 4 positions at a time.  Shapes or
+// pointers outside that form go through epilogue_scalar (same arithmetic per element).
+template <typename T, int EPI>
+__device__ void epilogue(const float* tile, int ldt, int rows, int m0, int vc0, int M, int Nv,
+                         const EpiArgs& e) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if constexpr (EPI == EPI_STORE || EPI == EPI_F32 || EPI == EPI_RESID) {
+    using O = typename std::conditional<EPI == EPI_STORE, T, float>::type;
+    O* y = (O*)e.y;
+    const bool vec = e.ldy % 4 == 0 && aligned_to(y, 4 * (int)sizeof(O));
+    for (int i = tid; i < rows * 32; i += nt) {
+      const int r = i >> 5, c = 4 * (i & 31);
+      const int m = m0 + r, vc = vc0 + c;
+      if (m >= M || vc >= Nv) continue;
+      const float4 v = *reinterpret_cast<const float4*>(tile + r * ldt + c);
+      O* p = y + (int64_t)m * e.ldy + vc;
+      if (vec && vc + 3 < Nv) {
+        if constexpr (EPI == EPI_STORE) {
+          store4<O>(p, v.x, v.y, v.z, v.w);
+        } else if constexpr (EPI == EPI_F32) {
+          store4<float>(p, v.x * e.scale, v.y * e.scale, v.z * e.scale, v.w * e.scale);
+        } else {
+          float4 o = *reinterpret_cast<const float4*>(p);
+          o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+          *reinterpret_cast<float4*>(p) = o;
+        }
+      } else {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        for (int u = 0; u < 4 && vc + u < Nv; ++u) {
+          if constexpr (EPI == EPI_STORE) Elt<O>::store(p, u, vv[u]);
+          else if constexpr (EPI == EPI_F32) p[u] = vv[u] * e.scale;
+          else p[u] += vv[u];
+        }
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int t = vc0 >> 7;
+    T* y = (T*)e.y;
+    if (e.F % 4 != 0 || !aligned_to(y, 4 * (int)sizeof(T))) {
+      epilogue_scalar<T, EPI>(tile, ldt, rows, m0, vc0, M, Nv, e);
+      return;
+    }
+    for (int i = tid; i < rows * 16; i += nt) {
+      const int r = i >> 4, c = 4 * (i & 15);
+      const int m = m0 + r, col = t * 64 + c;
+      if (m >= M || col >= e.F) continue;
+      const float4 gt = *reinterpret_cast<const float4*>(tile + r * ldt + c);
+      const float4 up = *reinterpret_cast<const float4*>(tile + r * ldt + 64 + c);
+      store4<T>(y + (int64_t)m * e.F + col, silu(gt.x) * up.x, silu(gt.y) * up.y,
+                silu(gt.z) * up.z, silu(gt.w) * up.w);
+    }
+  } else {  // EPI_QKV
+    const int D = e.D, half = D >> 1;
+    const int ab = 4 * (int)sizeof(T);
+    const bool vec = D >= 8 && (D & (D - 1)) == 0 && D <= 128 && rows >= 4 &&
+                     (rows & (rows - 1)) == 0 && aligned_to(e.qo, ab) &&
+                     aligned_to(e.kc, ab) && aligned_to(e.vtc, ab) && aligned_to(e.rcos, 16) &&
+                     aligned_to(e.rsin, 16);
+    if (!vec) {
+      epilogue_scalar<T, EPI>(tile, ldt, rows, m0, vc0, M, Nv, e);
+      return;
+    }
+    const int nqk = e.Hq + e.Hkv, lgD = ilog2(D);
+    // whole runs of 4 positions in one sequence and one 32-key block of the value cache
+    const bool v4 = e.R % 4 == 0 && e.pos0 % 4 == 0;
+    for (int cb = 0; cb < 128; cb += D) {  // the heads of the tile, D columns each
+      const int gh = (vc0 + cb) >> lgD;
+      if (vc0 + cb >= Nv) break;
+      if (gh < nqk) {
+        // q or k head: RoPE pairs (j, j + D/2), 4 adjacent j per thread
+        const int lgg = lgD - 3;  // log2 of the 4-wide groups per half (D/8)
+        for (int i = tid; i < (rows << lgg); i += nt) {
+          const int r = i >> lgg, j = 4 * (i & ((1 << lgg) - 1));
+          const int m = m0 + r;
+          if (m >= M) continue;
+          const int bs = m / e.R, ri = m - bs * e.R, pos = e.pos0 + ri;
+          const float4 x1 = *reinterpret_cast<const float4*>(tile + r * ldt + cb + j);
+          const float4 x2 = *reinterpret_cast<const float4*>(tile + r * ldt + cb + half + j);
+          const float4 cs = *reinterpret_cast<const float4*>(e.rcos + (int64_t)pos * half + j);
+          const float4 sn = *reinterpret_cast<const float4*>(e.rsin + (int64_t)pos * half + j);
+          T* dst;
+          if (gh < e.Hq) dst = (T*)e.qo + (((int64_t)bs * e.Hq + gh) * e.R + ri) * D;
+          else dst = (T*)e.kc + (((int64_t)bs * e.Hkv + (gh - e.Hq)) * e.Sp + pos) * D;
+          store4<T>(dst + j, x1.x * cs.x - x2.x * sn.x, x1.y * cs.y - x2.y * sn.y,
+                    x1.z * cs.z - x2.z * sn.z, x1.w * cs.w - x2.w * sn.w);
+          store4<T>(dst + j + half, x2.x * cs.x + x1.x * sn.x, x2.y * cs.y + x1.y * sn.y,
+                    x2.z * cs.z + x1.z * sn.z, x2.w * cs.w + x1.w * sn.w);
+        }
+      } else {
+        // value head: transposed, 32-key-blocked cache; consecutive threads take
+        // consecutive runs of 4 positions of one dim
+        const int h = gh - nqk;
+        const int lgn = ilog2(rows) - 2;  // log2 of the runs of 4 rows
+        for (int i = tid; i < (rows >> 2) * D; i += nt) {
+          const int d = i >> lgn, r = 4 * (i & ((1 << lgn) - 1));
+          const int m = m0 + r;
+          if (m >= M) continue;
+          if (v4 && m + 3 < M) {
+            const int bs = m / e.R, ri = m - bs * e.R, pos = e.pos0 + ri;
+            T* dst = (T*)e.vtc + ((int64_t)bs * e.Hkv + h) * D * (int64_t)e.Sp;
+            store4<T>(dst + vt_off(d, pos, D), tile[r * ldt + cb + d],
+                      tile[(r + 1) * ldt + cb + d], tile[(r + 2) * ldt + cb + d],
+                      tile[(r + 3) * ldt + cb + d]);
+          } else {
+            for (int u = 0; u < 4 && m + u < M; ++u) {
+              const int mu = m + u, bs = mu / e.R, pos = e.pos0 + (mu - bs * e.R);
+              T* dst = (T*)e.vtc + ((int64_t)bs * e.Hkv + h) * D * (int64_t)e.Sp;
+              Elt<T>::store(dst, vt_off(d, pos, D), tile[(r + u) * ldt + cb + d]);
+            }
+          }
+        }
       }
     }
   }
@@ -421,8 +556,9 @@ constexpr int BG_THREADS = 512;
 constexpr int BG_DK = 64, BG_NSTG = 2;                      // K per stage, ring slots
 static_assert(BG_NSTG <= 4, "the wait counts cover at most two stages in flight");
 constexpr int BG_AB_BYTES = BG_NSTG * 2 * BG_T * BG_DK * 2;  // ring of A and B stages
-constexpr int BG_TILE_BYTES = 128 * TL * 4;                 // one 128x128 quarter, fp32
+constexpr int BG_TILE_BYTES = 2 * 128 * TL * 4;             // two 128x128 quarters, fp32
 constexpr int BG_SMEM = BG_AB_BYTES > BG_TILE_BYTES ? BG_AB_BYTES : BG_TILE_BYTES;
+static_assert(BG_SMEM <= 160 * 1024, "LDS budget");
 
 // Column tiles tn0 + blockIdx.x.  With splits > 1 the tile's K piece is stored as fp32
 // partials [split][M][Nv - vbase] at column vc - vbase.
@@ -540,10 +676,11 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
 #undef DLLM_VMWAIT
   __syncthreads();  // the epilogue tile below reuses the operand slots
 
-  // epilogue, one 128x128 quarter (two waves) at a time
-  for (int p = 0; p < 4; ++p) {
-    const int qm = p >> 1, qn = p & 1;  // quarter rows 128 qm, columns 128 qn
-    if (wm == qm && (wn >> 1) == qn) {
+  // epilogue in two halves of 128 rows: the four waves of a half stage its two 128x128
+  // quarters side by side in LDS, then every thread works through them
+  for (int qm = 0; qm < 2; ++qm) {
+    if (wm == qm) {
+      float* t = tile + (wn >> 1) * 128 * TL;
       const int c0 = (wn & 1) * 64;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -551,20 +688,33 @@ __global__ __launch_bounds__(BG_THREADS, 1) void gemm_big_bf16(
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            tile[(i * 32 + acc_row(v, g)) * TL + c0 + j * 32 + lr] = acc[i][j][v];
+            t[(i * 32 + acc_row(v, g)) * TL + c0 + j * 32 + lr] = acc[i][j][v];
     }
     __syncthreads();
-    const int pm0 = m0 + 128 * qm, pvc0 = vc0 + 128 * qn;
-    if (splits == 1) {
-      epilogue<uint16_t, EPI>(tile, TL, 128, pm0, pvc0, M, Nv, e);
-    } else {
-      // split over K: partials summed in split order by the next RMSNorm (residual
-      // GEMMs) or by reduce_epilogue (a split tail of tiles)
-      const int Np = Nv - vbase;
-      for (int i = tid; i < 128 * 128; i += BG_THREADS) {
-        const int r = i >> 7, c = i & 127;
-        const int m = pm0 + r, vc = pvc0 + c;
-        if (m < M && vc < Nv) part[((int64_t)split * M + m) * Np + (vc - vbase)] = tile[r * TL + c];
+    const int pm0 = m0 + 128 * qm;
+    for (int qn = 0; qn < 2; ++qn) {
+      const float* t = tile + qn * 128 * TL;
+      const int pvc0 = vc0 + 128 * qn;
+      if (splits == 1) {
+        epilogue<uint16_t, EPI>(t, TL, 128, pm0, pvc0, M, Nv, e);
+      } else {
+        // split over K: partials summed in split order by the next RMSNorm (residual
+        // GEMMs) or by reduce_epilogue (a split tail of tiles), 4 columns per store
+        const int Np = Nv - vbase;
+        const bool vec = Np % 4 == 0;
+        for (int i = tid; i < 128 * 32; i += BG_THREADS) {
+          const int r = i >> 5, c = 4 * (i & 31);
+          const int m = pm0 + r, vc = pvc0 + c;
+          if (m >= M || vc >= Nv) continue;
+          float* dst = part + ((int64_t)split * M + m) * Np + (vc - vbase);
+          const float4 v = *reinterpret_cast<const float4*>(t + r * TL + c);
+          if (vec && vc + 3 < Nv) {
+            *reinterpret_cast<float4*>(dst) = v;
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+            for (int u = 0; u < 4 && vc + u < Nv; ++u) dst[u] = vv[u];
+          }
+        }
       }
     }
     __syncthreads();
@@ -601,13 +751,24 @@ static_assert(BG_T == kBigTile, "large tile edge");
 template <int EPI>
 __device__ void mid_epilogue(const float* tile, int M, int vc0, int Nv, const EpiArgs& e) {
   if constexpr (EPI == EPI_SWIGLU) {
-    // 64 outputs per row: column c of the tile's span takes gate 64(c/32) + c%32, up +32
-    for (int i = threadIdx.x; i < kMidRows * 64; i += blockDim.x) {
-      const int m = i >> 6, c = i & 63;
+    // 64 outputs per row: column c of the tile's span takes gate 64(c/32) + c%32, up +32;
+    // 4 adjacent outputs per thread
+    uint16_t* y = (uint16_t*)e.y;
+    const bool vec = e.F % 4 == 0 && aligned_to(y, 8);
+    for (int i = threadIdx.x; i < kMidRows * 16; i += blockDim.x) {
+      const int m = i >> 4, c = 4 * (i & 15);
       const int vg = 64 * (c >> 5) + (c & 31);
       if (m >= M || vc0 + vg >= Nv) continue;
-      ((uint16_t*)e.y)[(int64_t)m * e.F + vc0 / 2 + c] =
-          swiglu_bf16(tile[m * MD_TL + vg], tile[m * MD_TL + vg + 32]);
+      const float4 gt = *reinterpret_cast<const float4*>(tile + m * MD_TL + vg);
+      const float4 up = *reinterpret_cast<const float4*>(tile + m * MD_TL + vg + 32);
+      uint16_t* p = y + (int64_t)m * e.F + vc0 / 2 + c;
+      if (vec && vc0 + vg + 3 < Nv) {
+        *reinterpret_cast<u16x4*>(p) = u16x4{swiglu_bf16(gt.x, up.x), swiglu_bf16(gt.y, up.y),
+                                             swiglu_bf16(gt.z, up.z), swiglu_bf16(gt.w, up.w)};
+      } else {
+        const float gg[4] = {gt.x, gt.y, gt.z, gt.w}, uu[4] = {up.x, up.y, up.z, up.w};
+        for (int u = 0; u < 4 && vc0 + vg + u < Nv; ++u) p[u] = swiglu_bf16(gg[u], uu[u]);
+      }
     }
   } else if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
     epilogue<uint16_t, EPI>(tile, MD_TL, kMidRows, 0, vc0, M, Nv, e);
