@@ -110,6 +110,16 @@ def test_tiny_fp32_teacher_forced(lib, mode, tau):
         assert st["multi"] >= 2, "no step decoded several tokens"
 
 
+@pytest.mark.parametrize("mode,P", [("dual", 13), ("prefix", 13), ("dual", 18)])
+def test_tiny_fp32_teacher_forced_ragged_prompt(lib, mode, P):
+    """Prompt lengths that are not a multiple of 4: block positions and the sequence
+    length S are then not in runs of 4, so the GEMM epilogues write the value cache and
+    the RoPE'd rows element by element (the fallback of the 4-wide epilogue)."""
+    wl = replace(synth.WORKLOADS["tiny_dual"], cache_mode=mode, prompt_len=P)
+    st = teacher_forced(lib, wl, 1e-4, CONF_TOL_F32)
+    assert st["steps"] >= wl.gen_len // wl.block_len
+
+
 def free_running_compare(got, gspb, want, ospb, unsafe_blocks, K, n_blocks):
     """Blocks compared in order while every step of every earlier block (and the block
     itself) took decisions that cannot flip: identical tokens and steps per block.  The
@@ -203,9 +213,13 @@ def small_bf16(Hq=2, Hkv=2, mode="dual", B=2, P=40, G=64, K=32, V=2048, gain=0.1
 
 @pytest.mark.parametrize("Hq,Hkv,mode,B,K,P", [(2, 2, "dual", 2, 32, 40), (4, 1, "dual", 3, 16, 40),
                                              (2, 2, "prefix", 2, 32, 40), (2, 1, "prefix", 1, 8, 40),
-                                             (2, 1, "dual", 2, 32, 400)])
+                                             (2, 1, "dual", 2, 32, 400), (2, 1, "dual", 2, 32, 37),
+                                             (2, 2, "prefix", 1, 16, 45),
+                                             (2, 1, "dual", 2, 32, 401)])
 def test_small_bf16_teacher_forced(lib, Hq, Hkv, mode, B, K, P):
-    # P = 400: B * S = 928 rows, so the refresh runs the large-tile GEMM path
+    # P = 400: B * S = 928 rows, so the refresh runs the large-tile GEMM path; P = 37, 45
+    # and 401 put the block positions and S off runs of 4 (element-by-element value-cache
+    # and RoPE writes in the epilogues, on the mid, tiled and large-tile kernels)
     wl = small_bf16(Hq, Hkv, mode, B=B, K=K, P=P)
     st = teacher_forced(lib, wl, 2e-2)
     # bf16 logits differ by ~5e-3 relative, which moves confidences by up to
