@@ -21,6 +21,8 @@
 //   C: column l%32, rows 8*(v/4) + 4g + (v%4) for accumulator element v = 0..15.
 // Any consistent k permutation is valid for A and B; the P^T operand uses the
 // accumulator's own row order, and the Vt operand reads the same keys.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -105,6 +107,63 @@ __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
 // then m [32] and l [32].
 constexpr int kPartStride = 32 * HD + 64;
 
+// The products of one 32-key sub-tile (keys key0 ..) for 32 query rows (two 16-row tiles;
+// lane (l%16, j = l/16)), folded into the rows' online-softmax state (O^T unnormalised,
+// running maximum m and sum l, in the base-2 exponent domain of scale_log2).
+__device__ __forceinline__ void consume_subtile(const KVTile16& t, int key0,
+                                                const u32x4 (&qf)[2][4], f32x4 (&oacc)[2][8],
+                                                float (&m_run)[2], float (&l_run)[2], int S,
+                                                float scale_log2, int j) {
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    f32x4 sc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      sc[tau] = f32x4{};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        sc[tau] = mfma16(as_bf16x8(t.k[tau][st]), as_bf16x8(qf[qq][st]), sc[tau]);
+    }
+    // lane's 8 scores: keys key0 + 8j + e, e = 4 tau + r
+    float p[8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (key0 + 8 * j + e < S) ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+      p[e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = xor32_combine(xor16_combine(mx, fmax_op), fmax_op);
+    const float m_new = fmaxf(m_run[qq], mx);
+    // a sub-tile with no valid key at all leaves the state unchanged
+    const float alpha = (m_new == -INFINITY || m_run[qq] == -INFINITY)
+                            ? ((m_new == -INFINITY) ? 1.f : 0.f)
+                            : __builtin_amdgcn_exp2f(m_run[qq] - m_new);
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      p[e] = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[e] - m_new);
+      ls += p[e];
+    }
+    ls = xor32_combine(xor16_combine(ls, add_op), add_op);
+    l_run[qq] = l_run[qq] * alpha + ls;
+    m_run[qq] = m_new;
+    u16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[e] = f2bf(p[e]);
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pb);
+    // keys >= S: their P is 0, and their Vt values (read from clamped or padding
+    // positions) are zeroed so that no stale NaN/Inf reaches the product
+    const bool tail = key0 + 32 > S;  // uniform over the wave
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      oacc[qq][dt] *= alpha;
+      const u32x4 vv = tail ? mask8(t.v[dt], S - (key0 + 8 * j)) : t.v[dt];
+      oacc[qq][dt] = mfma16(as_bf16x8(vv), pop, oacc[qq][dt]);
+    }
+  }
+}
+
 // ONE: every wave has a single 32-key sub-tile (nsub == 1): one operand tile in
 // registers, so two workgroups fit on a CU.
 template <int NW, bool ONE>
@@ -164,54 +223,7 @@ __global__ __launch_bounds__(NW * 64, ONE ? 2 : 1) void attn_splitkv_bf16(
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
   auto consume = [&](const KVTile16& t, int key0) {
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      f32x4 sc[2];
-#pragma unroll
-      for (int tau = 0; tau < 2; ++tau) {
-        sc[tau] = f32x4{};
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-          sc[tau] = mfma16(as_bf16x8(t.k[tau][st]), as_bf16x8(qf[qq][st]), sc[tau]);
-      }
-      // lane's 8 scores: keys key0 + 8j + e, e = 4 tau + r
-      float p[8];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (key0 + 8 * j + e < S) ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
-        p[e] = x;
-        mx = fmaxf(mx, x);
-      }
-      mx = xor32_combine(xor16_combine(mx, fmax_op), fmax_op);
-      const float m_new = fmaxf(m_run[qq], mx);
-      // a sub-tile with no valid key at all leaves the state unchanged
-      const float alpha = (m_new == -INFINITY || m_run[qq] == -INFINITY)
-                              ? ((m_new == -INFINITY) ? 1.f : 0.f)
-                              : __builtin_amdgcn_exp2f(m_run[qq] - m_new);
-      float ls = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p[e] = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[e] - m_new);
-        ls += p[e];
-      }
-      ls = xor32_combine(xor16_combine(ls, add_op), add_op);
-      l_run[qq] = l_run[qq] * alpha + ls;
-      m_run[qq] = m_new;
-      u16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = f2bf(p[e]);
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pb);
-      // keys >= S: their P is 0, and their Vt values (read from clamped or padding
-      // positions) are zeroed so that no stale NaN/Inf reaches the product
-      const bool tail = key0 + 32 > S;  // uniform over the wave
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        oacc[qq][dt] *= alpha;
-        const u32x4 vv = tail ? mask8(t.v[dt], S - (key0 + 8 * j)) : t.v[dt];
-        oacc[qq][dt] = mfma16(as_bf16x8(vv), pop, oacc[qq][dt]);
-      }
-    }
+    consume_subtile(t, key0, qf, oacc, m_run, l_run, S, scale_log2, j);
   };
 
   if constexpr (ONE) {
@@ -327,6 +339,134 @@ __global__ __launch_bounds__(NW * 64, ONE ? 2 : 1) void attn_splitkv_bf16(
     if (d4 == 0) {
       pc[32 * HD + qi] = Mq[it];
       pc[32 * HD + 32 + qi] = Lq[it];
+    }
+  }
+}
+
+// ============================================================================
+// Grouped-query step attention (G = Hq / Hkv query heads per KV head, 2 <= G <= 8, at
+// most 32 query rows): grid (nchunk, B * Hkv), 8 waves.  Wave w < G takes query head
+// hkv * G + w through every 32-key sub-tile of the chunk; the chunk's K and Vt are read
+// from memory once per KV head into LDS (direct global->LDS loads) instead of once per
+// query head, and each wave reads them from there in the split-KV kernel's operand
+// layout.  Each wave writes its head's chunk result (O, m, l) in attn_combine's layout,
+// or, with a single chunk, the normalised output.
+//   LDS per 32-key sub-tile: K [32 keys][256 B] with 16-byte chunk c of key r at
+//   c ^ ((r % 4) + 4 (r / 8)), then Vt [128 dims][64 B] with chunk c of dim d at
+//   c ^ ((d / 4) % 4): the operand reads (16 rows at one chunk per LDS clock) are then
+//   conflict free.
+// ============================================================================
+constexpr int GQ_SUB = 16 * 1024;   // LDS bytes per 32-key sub-tile (K 8 KB, Vt 8 KB)
+constexpr int GQ_MAXSUB = 8;        // at most 256 keys per chunk (128 KB of LDS)
+
+__device__ __forceinline__ int gq_kswz(int r) { return (r & 3) | ((r >> 3) << 2); }
+
+__global__ __launch_bounds__(512, 1) void attn_gqa_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
+    int Sp, int nchunk, int ck, float scale_log2, float* __restrict__ part) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
+  const int chunk = blockIdx.x, b = blockIdx.y / Hkv, hkv = blockIdx.y % Hkv;
+  const int G = Hq / Hkv;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & 63, li = l & 15, j = l >> 4;
+  const int key_lo = chunk * ck;
+  const int nsub = (min(ck, S - key_lo) + 31) / 32;  // sub-tiles with a key below S
+
+  // Q^T operands of this wave's head: query 16 qq + li, dims 32 st + 8j .. +8 (rows >= R
+  // clamped: computed, never stored; waves w >= G load head G - 1 and stay idle)
+  const int hq = hkv * G + min(w, G - 1);
+  const uint16_t* qh = q + ((int64_t)b * Hq + hq) * R * HD;
+  u32x4 qf[2][4];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      qf[qq][st] = *reinterpret_cast<const u32x4*>(qh + (int64_t)min(16 * qq + li, R - 1) * HD +
+                                                   32 * st + 8 * j);
+
+  // the chunk's K and Vt: 16 loads of 1 KB per sub-tile (8 of K: 4 keys each; 8 of Vt: 16
+  // dims each), dealt to the waves in turn; keys past S read key S - 1 (masked scores),
+  // Vt chunks past Sp the last valid chunk (masked values)
+  const uint16_t* kb = k + ((int64_t)b * Hkv + hkv) * Sp * HD;
+  const uint16_t* vb = vt + ((int64_t)b * Hkv + hkv) * HD * Sp;
+  for (int i = w; i < nsub * 16; i += 8) {
+    const int sub = i >> 4, pc = i & 15;
+    unsigned char* base = gsm + sub * GQ_SUB;
+    const int key0 = key_lo + 32 * sub;
+    const uint16_t* src;
+    unsigned char* dst;
+    if (pc < 8) {
+      const int r = 4 * pc + (l >> 4), c = (l & 15) ^ gq_kswz(r);
+      src = kb + (int64_t)min(key0 + r, S - 1) * HD + 8 * c;
+      dst = base + pc * 1024;
+    } else {
+      const int d = 16 * (pc - 8) + (l >> 2), c = (l & 3) ^ ((d >> 2) & 3);
+      src = vb + vt_off(d, min(key0 + 8 * c, Sp - 8), HD);
+      dst = base + 8192 + (pc - 8) * 1024;
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt((0 & 15) | ((0 >> 4) << 14) | (7 << 4) | (15 << 8));  // vmcnt(0)
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  if (w >= G) return;  // no barrier follows
+
+  f32x4 oacc[2][8];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[qq][dt] = f32x4{};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  for (int sub = 0; sub < nsub; ++sub) {
+    const unsigned char* base = gsm + sub * GQ_SUB;
+    KVTile16 t;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      const int r = 8 * (li >> 2) + 4 * tau + (li & 3);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        t.k[tau][st] = *reinterpret_cast<const u32x4*>(
+            base + r * (HD * 2) + (((4 * st + j) ^ gq_kswz(r)) * 16));
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const int d = 16 * dt + li;
+      t.v[dt] = *reinterpret_cast<const u32x4*>(base + 8192 + d * 64 + ((j ^ ((d >> 2) & 3)) * 16));
+    }
+    consume_subtile(t, key_lo + 32 * sub, qf, oacc, m_run, l_run, S, scale_log2, j);
+  }
+
+  // lane holds query 16 qq + li, dims 16 dt + 4j .. +4
+  if (nchunk == 1) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int row = 16 * qq + li;
+      if (row >= R) continue;
+      const float inv = 1.0f / l_run[qq];
+      uint16_t* orow = o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        u16x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = f2bf(oacc[qq][dt][e] * inv);
+        *reinterpret_cast<u16x4*>(orow + 16 * dt + 4 * j) = r;
+      }
+    }
+    return;
+  }
+  float* pcb = part + ((int64_t)(b * Hq + hq) * nchunk + chunk) * kPartStride;
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qi = 16 * qq + li;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<float4*>(pcb + qi * HD + 16 * dt + 4 * j) =
+          make_float4(oacc[qq][dt][0], oacc[qq][dt][1], oacc[qq][dt][2], oacc[qq][dt][3]);
+    if (j == 0) {
+      pcb[32 * HD + qi] = m_run[qq];
+      pcb[32 * HD + 32 + qi] = l_run[qq];
     }
   }
 }
@@ -591,7 +731,19 @@ constexpr int kMaxChunks = 64;
 //  * else one sub-tile per wave in four-wave workgroups if that needs at most 512;
 //  * else four waves walking several sub-tiles each (a register-heavy kernel, one
 //    workgroup per CU), with chunks sized for about 256 workgroups.
-AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
+// Keys per chunk of the grouped-query kernel (a multiple of 32, at most 256 for its LDS),
+// chosen for about 256 workgroups of B * Hkv * chunks: every wave walks all sub-tiles of
+// its chunk, so shorter chunks and more workgroups (7B batch-8 step: 6.88 -> 6.75 ms with
+// 128-key chunks against 256); 0 where the kernel does not apply (more than 32 rows or
+// another head dim).
+static int gqa_chunk_keys(int B, int Hkv, int R, int S, int D) {
+  if (R > 32 || D != HD || B * Hkv < 1) return 0;
+  const int nchunk = (256 + B * Hkv - 1) / (B * Hkv);
+  const int ck = 32 * ((S + 32 * nchunk - 1) / (32 * nchunk));
+  return std::min(std::max(ck, 32), 32 * GQ_MAXSUB);
+}
+
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int R, int S, int D) {
   AttnPlan p;
   if (dtype == F32) { p.kind = 0; return p; }
   if (R <= 64) {
@@ -612,11 +764,27 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D) {
       p.nw = 4; p.nsub = ck / 128; p.nchunk = (S + ck - 1) / ck;
     }
     if (p.nchunk > 1) p.part_floats = (size_t)base * p.nchunk * kPartStride;
+    // grouped query heads: each chunk's K and Vt read once per KV head
+    const int G = (Hkv > 0 && Hq % Hkv == 0) ? Hq / Hkv : 1;
+    const int ck = (G >= 2 && G <= 8) ? gqa_chunk_keys(B, Hkv, R, S, D) : 0;
+    if (ck > 0) {
+      p.kind = 3;
+      p.ck = ck;
+      p.nchunk = (S + ck - 1) / ck;
+      p.part_floats = p.nchunk > 1 ? (size_t)base * p.nchunk * kPartStride : 0;
+    }
   } else {
     p.kind = 2;
     p.nqt = (R + 127) / 128;
   }
   return p;
+}
+
+size_t attn_part_floats_any_hkv(int dtype, int B, int Hq, int R, int S, int D) {
+  size_t n = attn_plan(dtype, B, Hq, Hq, R, S, D).part_floats;
+  for (int G = 2; G <= 8; ++G)
+    if (Hq % G == 0) n = std::max(n, attn_plan(dtype, B, Hq, Hq / G, R, S, D).part_floats);
+  return n;
 }
 
 hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const void* k,
@@ -644,6 +812,25 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
     else if (p.nw == 4) DLLM_ATTN(4, false);
     else return hipErrorInvalidValue;  // the plan never asks for 8 waves x several sub-tiles
 #undef DLLM_ATTN
+    if (p.nchunk > 1) {
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      attn_combine<<<dim3((unsigned)(B * Hq * p.nqt), 32 / kCombRows), 32 * kCombRows, 0, st>>>(
+          part, (uint16_t*)o, Hq, R, p.nqt, p.nchunk);
+    }
+  } else if (p.kind == 3) {
+    if (p.nchunk > 1 && !part) return hipErrorInvalidValue;
+    static bool attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
+    if (!attr_set) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_gqa_bf16),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           GQ_MAXSUB * GQ_SUB);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+    attn_gqa_bf16<<<dim3(p.nchunk, B * Hkv), 512, (p.ck / 32) * GQ_SUB, st>>>(
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
+        S, Sp, p.nchunk, p.ck, scale_log2, part);
     if (p.nchunk > 1) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;

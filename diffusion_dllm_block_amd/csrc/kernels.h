@@ -149,13 +149,18 @@ hipError_t launch_reduce_epilogue(int epi, const PartView& pv, const EpiArgs& e,
 
 // ---------------------------------------------------------------- attention
 struct AttnPlan {
-  int kind = 0;          // 0: fp32 simple, 1: bf16 split-KV (R <= 64), 2: bf16 flash
+  int kind = 0;          // 0: fp32 simple, 1: bf16 split-KV (R <= 64), 2: bf16 flash,
+                         // 3: bf16 grouped-query split-KV (R <= 32, 2 <= Hq/Hkv <= 8)
   int nqt = 0, nchunk = 0, nsub = 0;
+  int ck = 0;            // grouped-query: keys per chunk
   int nw = 4;            // split-KV: waves per workgroup (4 or 8)
   size_t part_floats = 0;
   int counters = 0;      // unused: chunk partials are merged by a second kernel
 };
-AttnPlan attn_plan(int dtype, int B, int Hq, int R, int S, int D);
+AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int R, int S, int D);
+// Partial floats of the attention plan for the largest need over every Hkv dividing Hq
+// (the grouped-query plan may use more, shorter chunks than the plan for Hkv = Hq).
+size_t attn_part_floats_any_hkv(int dtype, int B, int Hq, int R, int S, int D);
 hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const void* k,
                             const void* vt, void* o, int B, int Hq, int Hkv, int R, int S,
                             int Sp, int D, float* part, int* counters, hipStream_t st);

@@ -188,7 +188,7 @@ Ws plan_ws(const Dims& d) {
   for (int b = 0; b < d.nblocks; ++b) {
     int R = step_rows(d, b);
     plan_gemms(d, d.B * R, true, &gpf, &gcn);
-    AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, R, d.S, d.D);
+    AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, d.Hkv, R, d.S, d.D);
     if (ap.part_floats > apf) apf = ap.part_floats;
     if (ap.counters > acn) acn = ap.counters;
     if (d.mode == DLLM_CACHE_DUAL) break;  // every block has the same row count
@@ -358,7 +358,7 @@ dllm_status run_layers(const Ctx& c, int r0, int R, bool refresh, int l0 = 0) {
     HIP_TRY(launch_embed_norm(d.dtype, c.s->tokens, d.S, r0, R, d.B, c.m->embed,
                               c.m->attn_norm[0], d.eps, d.d, d.V, x, h, c.st));
   }
-  AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, R, d.S, d.D);
+  AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, d.Hkv, R, d.S, d.D);
   if (ap.part_floats > c.w.apart_floats || ap.counters > c.w.acnt_n)
     return fail(DLLM_E_WORKSPACE, "internal: attention plan exceeds the workspace plan");
   const int Nqkv = (d.Hq + 2 * d.Hkv) * d.D;
@@ -759,9 +759,11 @@ dllm_status dllm_generate_graphs(const dllm_model_desc* m, const dllm_seq_desc* 
 }
 
 // ---------------------------------------------------------------- kernel-level entries
-static size_t kw_attn(int B, int Hq, int R, int S, int D, int dtype, AttnPlan* p) {
-  *p = attn_plan(dtype, B, Hq, R, S, D);
-  return up((size_t)p->counters * 4) + up(p->part_floats * 4);
+// Workspace of the attention entry: the plan's counters and partials, the partials sized
+// for every Hkv dividing Hq, since the workspace query does not take Hkv.
+static size_t kw_attn(int B, int Hq, int Hkv, int R, int S, int D, int dtype, AttnPlan* p) {
+  *p = attn_plan(dtype, B, Hq, Hkv, R, S, D);
+  return up((size_t)p->counters * 4) + up(attn_part_floats_any_hkv(dtype, B, Hq, R, S, D) * 4);
 }
 static size_t kw_conf(int rows, int V, int B, ConfPlan* p) {
   *p = conf_plan(rows, V, B);
@@ -773,7 +775,7 @@ size_t dllm_kernel_workspace_bytes(int32_t B, int32_t Hq, int32_t R, int32_t S, 
   AttnPlan ap;
   ConfPlan cp;
   if (B < 1) return 0;
-  size_t a = (Hq > 0 && R > 0 && S > 0 && D > 0) ? kw_attn(B, Hq, R, S, D, DLLM_BF16, &ap) : 0;
+  size_t a = (Hq > 0 && R > 0 && S > 0 && D > 0) ? kw_attn(B, Hq, Hq, R, S, D, DLLM_BF16, &ap) : 0;
   size_t c = (K > 0 && V > 0) ? kw_conf(B * K, V, B, &cp) : 0;
   return a > c ? a : c;
 }
@@ -793,7 +795,7 @@ dllm_status dllm_kernel_block_attention(const void* q, const void* k, const void
   if (dtype == DLLM_F32 && (D > 128 || S > 12000))
     return fail(DLLM_E_UNSUPPORTED, "fp32 attention needs D <= 128 and S <= 12000");
   AttnPlan p;
-  size_t need = kw_attn(B, Hq, R, S, D, dtype, &p);
+  size_t need = kw_attn(B, Hq, Hkv, R, S, D, dtype, &p);
   if (need && (!ws || ws_bytes < need)) return fail(DLLM_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, need);
   hipStream_t st = (hipStream_t)stream;
   int* cnt = (int*)ws;

@@ -227,9 +227,10 @@ dllm_status dllm_cache_staleness(const dllm_model_desc* m, const dllm_seq_desc* 
 /* ---- kernel-level entries (single stages on caller buffers) ---------------------- */
 
 /* Workspace needed by the two kernel-level calls below: the attention part for
- * (B, Hq, R, S, D) when all are positive, the confidence part for B sequences of K
- * block positions over a vocabulary of V when K and V are positive; the larger of the
- * two.  Returns 0 if B < 1.                                                          */
+ * (B, Hq, R, S, D) when all are positive (enough for any Hkv dividing Hq: with grouped
+ * query heads the attention may split the keys into more, shorter chunks), the
+ * confidence part for B sequences of K block positions over a vocabulary of V when K
+ * and V are positive; the larger of the two.  Returns 0 if B < 1.                    */
 size_t dllm_kernel_workspace_bytes(int32_t B, int32_t Hq, int32_t R, int32_t S, int32_t D,
                                    int32_t K, int32_t V);
 

@@ -187,12 +187,18 @@ ATTN_CASES = [
     ("llada_block32_kv2024", 1, 32, 32, 32, 2024, "bf16"),
     # eight-wave chunks whose last chunk has seven waves past the last key
     ("nw8_masked_waves", 1, 32, 32, 32, 1800, "bf16"),
+    # grouped query heads (one workgroup per KV head and chunk, a wave per query head):
+    # 32 chunks of one 32-key sub-tile, ragged last chunk
     ("gqa_7to1_b2", 2, 28, 4, 32, 1000, "bf16"),
-    # the 7B batch-8 step shape (eight-wave chunks, 896 workgroups)
+    # the 7B batch-8 step shape: 8 chunks of 128 keys, 256 workgroups
     ("gqa_7to1_b8", 8, 28, 4, 32, 1024, "bf16"),
-    # several sub-tiles per wave: 10 per wave over 2 chunks (GQA), 9 (odd) per wave over
-    # 4 chunks with a ragged last one
+    # 10 chunks of 256 keys (the LDS limit), ragged last one
     ("gqa_7to1_b8_multi_subtile", 8, 28, 4, 32, 2500, "bf16"),
+    # fewer rows than a tile, ragged keys, group of 4 (idle waves 4-7)
+    ("gqa_4to1_rows20_ragged", 2, 8, 2, 20, 777, "bf16"),
+    # a single chunk: the normalised output is written directly, no combine
+    ("gqa_2to1_one_chunk", 1, 4, 2, 32, 30, "bf16"),
+    # several sub-tiles per wave: 9 (odd) per wave over 4 chunks with a ragged last one
     ("multi_subtile_odd_ragged", 2, 32, 32, 32, 4400, "bf16"),
     # 17 eight-wave chunks: the merge walks its chunks in three rounds of loads
     ("many_chunks_ragged", 1, 32, 32, 32, 4100, "bf16"),
