@@ -727,7 +727,10 @@ constexpr int kMaxChunks = 64;
 
 // Step attention (at most 64 query rows), 32-key sub-tiles per wave:
 //  * one sub-tile per wave in eight-wave workgroups (256-key chunks: half the partials
-//    to merge of four-wave chunks) when that gives 256 to 1024 workgroups;
+//    to merge of four-wave chunks) when that gives 160 to 1024 workgroups (32 query rows
+//    x 32 heads against 1032-1500 keys, kernel-only: 14.4-15.7 us with 9-12 four-wave
+//    chunks per head, 13.9-14.3 with 5-6 eight-wave ones; with 4 eight-wave chunks, 128
+//    workgroups, 1024 keys took 13.4 against 13.0 us);
 //  * else one sub-tile per wave in four-wave workgroups if that needs at most 512;
 //  * else four waves walking several sub-tiles each (a register-heavy kernel, one
 //    workgroup per CU), with chunks sized for about 256 workgroups.
@@ -751,7 +754,7 @@ AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int R, int S, int D) {
     p.nqt = (R + 31) / 32;
     const int64_t base = (int64_t)B * Hq * p.nqt;
     const int n8 = (S + 255) / 256, n4 = (S + 127) / 128;
-    if (base * n8 >= 256 && base * n8 <= 1024 && n8 <= kMaxChunks) {
+    if (base * n8 >= 160 && base * n8 <= 1024 && n8 <= kMaxChunks) {
       p.nw = 8; p.nsub = 1; p.nchunk = n8;
     } else if (base * n4 <= 512 && n4 <= kMaxChunks) {
       p.nw = 4; p.nsub = 1; p.nchunk = n4;

@@ -187,6 +187,9 @@ ATTN_CASES = [
     ("llada_block32_kv2024", 1, 32, 32, 32, 2024, "bf16"),
     # eight-wave chunks whose last chunk has seven waves past the last key
     ("nw8_masked_waves", 1, 32, 32, 32, 1800, "bf16"),
+    # six eight-wave chunks (192 workgroups, the fewest that take this form); the last
+    # chunk holds 20 keys: one partial sub-tile and seven waves past the last key
+    ("nw8_six_chunks_ragged", 1, 32, 32, 32, 1300, "bf16"),
     # grouped query heads (one workgroup per KV head and chunk, a wave per query head):
     # 32 chunks of one 32-key sub-tile, ragged last chunk
     ("gqa_7to1_b2", 2, 28, 4, 32, 1000, "bf16"),
