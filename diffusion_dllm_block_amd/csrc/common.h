@@ -133,11 +133,21 @@ __device__ __forceinline__ int wave_min_dpp(int v) {
 // store carries sc1 and is acknowledged once it is visible to every XCD) and read back
 // with device-coherent loads.  A device-scope release/acquire fence would instead write
 // back and invalidate the whole L2 of the issuing XCD on every arrival.
+// The same stores also carry outputs that only the next kernel reads, from other XCDs:
+// written through, they leave no dirty lines for the end-of-kernel write-back (used
+// where that measured faster, see the callers).
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void st_dev(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// four bf16 values as one 8-byte device-coherent store (p 8-byte aligned)
+__device__ __forceinline__ void st_dev(uint16_t* p, u16x4 v) {
+  uint64_t bits;
+  __builtin_memcpy(&bits, &v, sizeof bits);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
