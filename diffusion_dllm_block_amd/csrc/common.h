@@ -142,6 +142,9 @@ __device__ __forceinline__ void st_dev(float* p, float v) {
 __device__ __forceinline__ void st_dev(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // four bf16 values as one 8-byte device-coherent store (p 8-byte aligned)
 __device__ __forceinline__ void st_dev(uint16_t* p, u16x4 v) {
   uint64_t bits;

@@ -1080,7 +1080,8 @@ __global__ __launch_bounds__(256) void reduce_epilogue(PartView pv, EpiArgs e, i
         uint16_t* dst = (uint16_t*)e.vtc +
                         ((int64_t)bs * e.Hkv + (hs - e.Hq - e.Hkv)) * 128 * (int64_t)e.Sp;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[vt_off(dbase + d0 + i, pos, 128)] = f2bf(tile[mr][d0 + i]);
+        // written through: the attention kernel that follows reads the cache from every XCD
+        for (int i = 0; i < 4; ++i) st_dev(&dst[vt_off(dbase + d0 + i, pos, 128)], f2bf(tile[mr][d0 + i]));
       }
       return;
     }
