@@ -359,39 +359,57 @@ def kernel_only(lib, torch, bd, rounds: int = 10):
     return out
 
 
-def ablation(model, wl, torch):
+def ablation(model, wl, torch, gen_lens=()):
     """The two halves of the method switched on one at a time, on the same model and
     prompts: no cache (every step a full forward) or the workload's cache, and one token
     per step (threshold 2 > 1: only the forced pick) or threshold decoding.  One timed
-    generation each after a warm-up of the cached configuration."""
+    generation each after a warm-up of the cached configuration.  With gen_lens, the same
+    four runs at each of those generation lengths (same prompt): the pages report the
+    cache's speed-up growing with the generation length."""
     from diffusion_dllm_block_amd.engine import Session
     prompt = synth.make_prompt(wl)
-    runs = [("no cache, one token per step", "none", 2.0),
-            ("no cache, parallel decoding", "none", wl.threshold),
-            (f"{wl.cache_mode} cache, one token per step", wl.cache_mode, 2.0),
-            (f"{wl.cache_mode} cache, parallel decoding (Fast-dLLM)", wl.cache_mode, wl.threshold)]
-    warm = Session(model, prompt, wl.gen_len, wl.block_len, wl.threshold, wl.cache_mode)
-    warm.generate()
-    del warm
-    out = []
-    for name, mode, tau in runs:
-        sess = Session(model, prompt, wl.gen_len, wl.block_len, tau, mode)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        _, st = sess.generate()
-        torch.cuda.synchronize()
-        dt = time.perf_counter() - t0
-        out.append({"config": name, "cache": mode, "threshold": tau,
-                    "tokens_per_s": round(wl.batch * wl.gen_len / dt, 2),
-                    "seconds": round(dt, 3), "steps": st["steps"],
-                    "full_forwards": st["refreshes"],
-                    "tokens_per_step": round(wl.batch * wl.gen_len / st["steps"], 3)})
-        log(f"ablation {name}: {dt:.2f} s, {st['steps']} steps, {st['refreshes']} full forwards")
-        del sess
-    base = out[0]["seconds"]
-    for r in out:
-        r["speedup_vs_no_cache_one_token"] = round(base / r["seconds"], 2)
-    return {"workload": wl.name, "runs": out}
+
+    def four(G):
+        runs = [("no cache, one token per step", "none", 2.0),
+                ("no cache, parallel decoding", "none", wl.threshold),
+                (f"{wl.cache_mode} cache, one token per step", wl.cache_mode, 2.0),
+                (f"{wl.cache_mode} cache, parallel decoding (Fast-dLLM)", wl.cache_mode,
+                 wl.threshold)]
+        warm = Session(model, prompt, G, wl.block_len, wl.threshold, wl.cache_mode)
+        warm.generate()
+        del warm
+        out = []
+        for name, mode, tau in runs:
+            sess = Session(model, prompt, G, wl.block_len, tau, mode)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            _, st = sess.generate()
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            out.append({"config": name, "cache": mode, "threshold": tau,
+                        "tokens_per_s": round(wl.batch * G / dt, 2),
+                        "seconds": round(dt, 3), "steps": st["steps"],
+                        "full_forwards": st["refreshes"],
+                        "tokens_per_step": round(wl.batch * G / st["steps"], 3)})
+            log(f"ablation G={G} {name}: {dt:.2f} s, {st['steps']} steps, "
+                f"{st['refreshes']} full forwards")
+            del sess
+        base = out[0]["seconds"]
+        for r in out:
+            r["speedup_vs_no_cache_one_token"] = round(base / r["seconds"], 2)
+        return out
+
+    res = {"workload": wl.name, "gen_len": wl.gen_len, "runs": four(wl.gen_len)}
+    trend = []
+    for G in gen_lens:
+        if G <= 0 or G % wl.block_len:
+            raise SystemExit(f"--ablation-gen-lens: {G} is not a positive multiple of the "
+                             f"block length {wl.block_len}")
+        runs = res["runs"] if G == wl.gen_len else four(G)
+        trend.append({"gen_len": G, "runs": runs})
+    if trend:
+        res["gen_len_trend"] = trend
+    return res
 
 
 def staleness_trace(sess, wl, blocks: int):
@@ -435,6 +453,9 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the kernel-only rates")
     ap.add_argument("--ablation", action="store_true",
                     help="cache on/off x parallel decoding on/off on the workload, one JSON line")
+    ap.add_argument("--ablation-gen-lens", default="",
+                    help="with --ablation: also run it at these generation lengths "
+                         "(comma-separated multiples of the block length)")
     ap.add_argument("--staleness", type=int, default=0, metavar="BLOCKS",
                     help="cache staleness before every cached step of the first BLOCKS "
                          "blocks, one JSON line (no timing)")
@@ -495,7 +516,8 @@ def main():
     log(f"weights + buffers ready in {time.time() - t:.1f} s")
     if a.ablation:
         del sess
-        print(json.dumps({"ablation": ablation(model, wl, torch)}), flush=True)
+        lens = [int(x) for x in a.ablation_gen_lens.split(",") if x.strip()]
+        print(json.dumps({"ablation": ablation(model, wl, torch, lens)}), flush=True)
         return
     if a.stage:
         sess.prefill()
