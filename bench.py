@@ -363,18 +363,22 @@ def ablation(model, wl, torch, gen_lens=()):
     """The two halves of the method switched on one at a time, on the same model and
     prompts: no cache (every step a full forward) or the workload's cache, and one token
     per step (threshold 2 > 1: only the forced pick) or threshold decoding.  One timed
-    generation each after a warm-up of the cached configuration.  With gen_lens, the same
-    four runs at each of those generation lengths (same prompt): the pages report the
-    cache's speed-up growing with the generation length."""
+    generation each after a warm-up of the cached configuration, plus the other cache
+    (prefix for a DualCache workload, and the reverse) with threshold decoding.  With
+    gen_lens, the first four runs at each of those generation lengths (same prompt): the
+    pages report the cache's speed-up growing with the generation length."""
     from diffusion_dllm_block_amd.engine import Session
     prompt = synth.make_prompt(wl)
 
-    def four(G):
+    def four(G, other_cache=False):
         runs = [("no cache, one token per step", "none", 2.0),
                 ("no cache, parallel decoding", "none", wl.threshold),
                 (f"{wl.cache_mode} cache, one token per step", wl.cache_mode, 2.0),
                 (f"{wl.cache_mode} cache, parallel decoding (Fast-dLLM)", wl.cache_mode,
                  wl.threshold)]
+        if other_cache:  # the other cache of the pages, same decoding rule
+            alt = "prefix" if wl.cache_mode == "dual" else "dual"
+            runs.append((f"{alt} cache, parallel decoding", alt, wl.threshold))
         warm = Session(model, prompt, G, wl.block_len, wl.threshold, wl.cache_mode)
         warm.generate()
         del warm
@@ -399,13 +403,13 @@ def ablation(model, wl, torch, gen_lens=()):
             r["speedup_vs_no_cache_one_token"] = round(base / r["seconds"], 2)
         return out
 
-    res = {"workload": wl.name, "gen_len": wl.gen_len, "runs": four(wl.gen_len)}
+    res = {"workload": wl.name, "gen_len": wl.gen_len, "runs": four(wl.gen_len, True)}
     trend = []
     for G in gen_lens:
         if G <= 0 or G % wl.block_len:
             raise SystemExit(f"--ablation-gen-lens: {G} is not a positive multiple of the "
                              f"block length {wl.block_len}")
-        runs = res["runs"] if G == wl.gen_len else four(G)
+        runs = res["runs"][:4] if G == wl.gen_len else four(G)
         trend.append({"gen_len": G, "runs": runs})
     if trend:
         res["gen_len_trend"] = trend
