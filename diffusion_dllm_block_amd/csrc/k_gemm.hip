@@ -306,8 +306,12 @@ template <int MT, int KS> struct SkinnyCfg {
   static constexpr int LDX = KW + 8;                 // LDS row stride (elements)
   static constexpr int XV = MT * 16 * KW / 8 / 512;  // 16-byte activation loads per thread
   static constexpr int SLOTS = MT * 4;               // result rows of 64 lanes per group
+  // the cross-wave sums go through LDS at most 8 result rows at a time, which leaves
+  // room for a 128-deep per-wave K range at 64 rows (64 x 24576 x 4096: 67.8 -> 48.6 us
+  // against a 64-deep one, whose 2 loads per lane in flight starved the weight stream)
+  static constexpr int RS = SLOTS < 8 ? SLOTS : 8;
   static_assert(XV >= 1, "activation slice smaller than one load per thread");
-  static_assert(MT * 16 * LDX * 2 + 8 * SLOTS * 64 * 4 <= 160 * 1024, "LDS budget");
+  static_assert(MT * 16 * LDX * 2 + 8 * RS * 64 * 4 <= 160 * 1024, "LDS budget");
 };
 
 template <int MAP, int MT, int KS>
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int K, int F, int splits, int ngrp, float* __restrict__ part) {
   using C = SkinnyCfg<MT, KS>;
   __shared__ __attribute__((aligned(16))) uint16_t Xs[MT * 16 * C::LDX];
-  __shared__ __attribute__((aligned(16))) float red[8][C::SLOTS][64];
+  __shared__ __attribute__((aligned(16))) float red[8][C::RS][64];
   const int split = blockIdx.x % splits;
   const int wid = blockIdx.x / splits;
   const int nw = gridDim.x / splits;  // workgroups per K range (grid is a multiple of splits)
@@ -385,19 +389,26 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       wr[t] = *reinterpret_cast<const u32x4*>(wpn + 32 * t);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // lane (column ln, group g) holds rows mt*16 + 4g + r: slot mt*4 + r
+    // lane (column ln, group g) holds rows mt*16 + 4g + r: slot mt*4 + r; the slots go
+    // through LDS RS at a time
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int h = 0; h < C::SLOTS / C::RS; ++h) {
+      if (h > 0) __syncthreads();  // red is rewritten by the next slots
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[w][mt * 4 + r][l] = acc[mt][r];
-    __syncthreads();
-    if (grp < ngrp) {
-      float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
-      for (int sl = w; sl < C::SLOTS; sl += 8) {
-        float v = red[0][sl][l];
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ww = 1; ww < 8; ++ww) v += red[ww][sl][l];
-        st_dev(&blk[sl * 64 + l], v);
+        for (int r = 0; r < 4; ++r)
+          if (mt * 4 + r >= h * C::RS && mt * 4 + r < (h + 1) * C::RS)
+            red[w][mt * 4 + r - h * C::RS][l] = acc[mt][r];
+      __syncthreads();
+      if (grp < ngrp) {
+        float* blk = part + ((int64_t)split * ngrp + grp) * (MT * 16 * 16);
+        for (int sl = w; sl < C::RS; sl += 8) {
+          float v = red[0][sl][l];
+#pragma unroll
+          for (int ww = 1; ww < 8; ++ww) v += red[ww][sl][l];
+          st_dev(&blk[(h * C::RS + sl) * 64 + l], v);
+        }
       }
     }
     __syncthreads();  // red is rewritten by the next group
@@ -1193,7 +1204,7 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     p.ntn = (Nv + 15) / 16;  // 16-column groups
     p.ntm = 1;
     // per-wave K sub-range KS (the workgroup covers 8 KS): among 256/128/64 with
-    // K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 64), the
+    // K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 128), the
     // largest that still gives every workgroup at least 4 of the 16-column groups to walk
     // (a workgroup with fewer spends most of its time staging its activation slice and
     // waiting for its first weights: the 8B output projection, 2 groups per workgroup at
@@ -1202,7 +1213,7 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     bool found = false;
     const int ngrp16 = (Nv + 15) / 16;
     for (int c : {256, 128, 64}) {
-      if (K % (8 * c) != 0 || (p.mt > 2 && c > 64)) continue;
+      if (K % (8 * c) != 0 || (p.mt > 2 && c > 128)) continue;
       const int per_range = std::max(1, num_cus() / (K / (8 * c)));  // workgroups per K range
       if (!found) { ks = c; found = true; }
       if (ngrp16 >= 4 * per_range) { ks = c; break; }
@@ -1376,7 +1387,8 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
       else if (ks == 64) DLLM_SKINNY(2, 64);
       else DLLM_SKINNY(2, 32);
     } else {
-      if (ks == 64) DLLM_SKINNY(4, 64);
+      if (ks == 128) DLLM_SKINNY(4, 128);
+      else if (ks == 64) DLLM_SKINNY(4, 64);
       else DLLM_SKINNY(4, 32);
     }
 #undef DLLM_SKINNY
