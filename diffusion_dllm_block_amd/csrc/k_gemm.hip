@@ -793,7 +793,7 @@ __device__ void mid_epilogue(const float* tile, int M, int vc0, int Nv, const Ep
   // residual and QKV GEMMs are always split (the plan gives them no whole tiles)
 }
 
-template <int MAP, int EPI>
+template <int MAP, int EPI, bool FULL>
 __global__ __launch_bounds__(MD_THREADS, 1) void gemm_mid_bf16(
     const uint16_t* __restrict__ X, int ldx, const uint16_t* __restrict__ W, int M, int Nv, int K,
     int ndp, int splits, int kst, int nunits, float* __restrict__ part, EpiArgs e) {
@@ -839,13 +839,15 @@ __global__ __launch_bounds__(MD_THREADS, 1) void gemm_mid_bf16(
       bsrc[i] = W + (int64_t)wrow_s2<MAP>(min(vc0 + row, Nv - 1), e.F) * K + kb +
                 ((l & 7) ^ swz(row)) * 8;
     }
-    // rows past M are neither loaded nor multiplied: wave w's activation loads cover rows
-    // 32w + 8i for i < nxi, and a wave whose 64-row band starts at or past M skips its
-    // MFMAs (bit-identical; 96 rows x 24576 x 4096: 80.3 -> 62.5 us, prefix workload
-    // 976 -> 956 ms per generation).  Rows past M that a band still covers read stale
-    // LDS rows; their results are never stored.
-    const int nxi = __builtin_amdgcn_readfirstlane(min(4, max(0, (M - 32 * w + 7) / 8)));
-    const bool act = 64 * wm < M;
+    // Below 256 rows (FULL false), rows past M are neither loaded nor multiplied: wave
+    // w's activation loads cover rows 32w + 8i for i < nxi, and a wave whose 64-row band
+    // starts at or past M skips its MFMAs (bit-identical; 96 rows x 24576 x 4096: 80.3 ->
+    // 62.5 us, prefix workload 976 -> 956 ms per generation).  Rows past M that a band
+    // still covers read stale LDS rows; their results are never stored.  At 256 rows the
+    // FULL instantiation has no such branches (they cost the 7B batch-8 step 1.4 %).
+    const int nxi =
+        FULL ? 4 : __builtin_amdgcn_readfirstlane(min(4, max(0, (M - 32 * w + 7) / 8)));
+    const bool act = FULL || 64 * wm < M;
     auto issue = [&](int st) {
       unsigned char* base = md_smem + (st % MD_NSTG) * MD_STG;
 #pragma unroll
@@ -1396,15 +1398,23 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
     constexpr int MAP = (EPI == EPI_SWIGLU || EPI == EPI_QKV) ? EPI : EPI_STORE;
     static bool mid_attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
     if (!mid_attr_set) {
-      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_mid_bf16<MAP, EPI>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, MD_SMEM);
-      if (err != hipSuccess) return err;
+      for (const void* f : {reinterpret_cast<const void*>(&gemm_mid_bf16<MAP, EPI, true>),
+                            reinterpret_cast<const void*>(&gemm_mid_bf16<MAP, EPI, false>)}) {
+        hipError_t err =
+            hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, MD_SMEM);
+        if (err != hipSuccess) return err;
+      }
       mid_attr_set = true;
     }
     const int grid = std::min(p.units, num_cus());
-    gemm_mid_bf16<MAP, EPI><<<grid, MD_THREADS, MD_SMEM, st>>>(
-        (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.ndp, p.splits,
-        p.kchunk / MD_DK, p.units, part, e);
+    if (M >= kMidRows)
+      gemm_mid_bf16<MAP, EPI, true><<<grid, MD_THREADS, MD_SMEM, st>>>(
+          (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.ndp, p.splits,
+          p.kchunk / MD_DK, p.units, part, e);
+    else
+      gemm_mid_bf16<MAP, EPI, false><<<grid, MD_THREADS, MD_SMEM, st>>>(
+          (const uint16_t*)X, ldx, (const uint16_t*)W, M, Nv, K, p.ndp, p.splits,
+          p.kchunk / MD_DK, p.units, part, e);
   } else if (p.kind == GEMM_BIG) {
     static bool attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
     if (!attr_set) {
