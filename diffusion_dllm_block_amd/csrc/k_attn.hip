@@ -525,7 +525,7 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
 }
 
 // ============================================================================
-// Flash attention over all rows (refresh, or prefix-mode steps with many rows):
+// Flash attention over all rows (refresh, or steps with more than 256 rows):
 // grid (ceil(R/128), Hq, B); wave w owns query rows qt*128 + w*32 .. +32; key tiles of
 // 64 staged in LDS and shared by the 4 waves; online softmax per query lane.
 // ============================================================================
@@ -728,7 +728,9 @@ __global__ __launch_bounds__(128) void attn_f32(const float* __restrict__ q,
 
 constexpr int kMaxChunks = 64;
 
-// Step attention (at most 64 query rows), 32-key sub-tiles per wave:
+// Step attention (at most 256 query rows: a block step, or the block and suffix rows of a
+// prefix-mode step, where the 128-row flash tiles would give only 32-64 workgroups; prefix
+// workload 926 -> 920 ms per generation), 32-row query tiles, 32-key sub-tiles per wave:
 //  * one sub-tile per wave in eight-wave workgroups (256-key chunks: half the partials
 //    to merge of four-wave chunks) when that gives 160 to 1024 workgroups (32 query rows
 //    x 32 heads against 1032-1500 keys, kernel-only: 14.4-15.7 us with 9-12 four-wave
@@ -752,7 +754,7 @@ static int gqa_chunk_keys(int B, int Hkv, int R, int S, int D) {
 AttnPlan attn_plan(int dtype, int B, int Hq, int Hkv, int R, int S, int D) {
   AttnPlan p;
   if (dtype == F32) { p.kind = 0; return p; }
-  if (R <= 64) {
+  if (R <= 256) {
     p.kind = 1;
     p.nqt = (R + 31) / 32;
     const int64_t base = (int64_t)B * Hq * p.nqt;

@@ -185,6 +185,11 @@ Ws plan_ws(const Dims& d) {
   size_t gpf = 0, apf = 0;
   int gcn = 0, acn = 0;
   plan_gemms(d, (int)Mmax, false, &gpf, &gcn);
+  {  // the refresh's attention (all S rows; short sequences take the split-KV kernel)
+    AttnPlan ap = attn_plan(d.dtype, d.B, d.Hq, d.Hkv, d.S, d.S, d.D);
+    apf = ap.part_floats;
+    acn = ap.counters;
+  }
   for (int b = 0; b < d.nblocks; ++b) {
     int R = step_rows(d, b);
     plan_gemms(d, d.B * R, true, &gpf, &gcn);

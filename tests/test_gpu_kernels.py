@@ -207,7 +207,10 @@ ATTN_CASES = [
     ("many_chunks_ragged", 1, 32, 32, 32, 4100, "bf16"),
     ("ragged_rows_keys", 1, 4, 2, 20, 77, "bf16"),
     ("two_row_tiles", 1, 2, 1, 64, 300, "bf16"),
-    ("flash_many_rows", 1, 2, 2, 200, 333, "bf16"),
+    # 200 query rows: seven 32-row query tiles on the split-KV kernel (prefix-mode steps)
+    ("split_kv_200_rows", 1, 2, 2, 200, 333, "bf16"),
+    # past 256 rows the flash kernel: three 128-row tiles, the last ragged
+    ("flash_300_rows", 1, 2, 2, 300, 333, "bf16"),
     ("flash_refresh_shape", 1, 4, 4, 2024, 2024, "bf16"),
     ("f32_small", 2, 4, 2, 8, 48, "f32"),
 ]
