@@ -1205,20 +1205,30 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     p.mt = (M <= 16) ? 1 : (M <= 32) ? 2 : 4;
     p.ntn = (Nv + 15) / 16;  // 16-column groups
     p.ntm = 1;
-    // per-wave K sub-range KS (the workgroup covers 8 KS): among 256/128/64 with
-    // K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 128), the
-    // largest that still gives every workgroup at least 4 of the 16-column groups to walk
-    // (a workgroup with fewer spends most of its time staging its activation slice and
-    // waiting for its first weights: the 8B output projection, 2 groups per workgroup at
-    // 256, runs 10.3 us at 256 and 8.4 us at 128), else the largest (32 if none)
+    // per-wave K sub-range KS (the workgroup covers 8 KS): among 256/192/128/64 with
+    // K % (8 KS) == 0 whose activation slice fits the LDS (M > 32 rows: KS <= 128), those
+    // that give every workgroup at least 4 of the 16-column groups to walk (a workgroup
+    // with fewer spends most of its time staging its activation slice and waiting for its
+    // first weights: the 8B output projection, 2 groups per workgroup at 256, runs
+    // 10.3 us at 256 and 8.4 us at 128) compete on the critical path, the most groups
+    // one workgroup walks times (KS + 64) (the 64 stands for a group's fixed cost: its
+    // cross-wave sum and partial stores), larger KS on ties; else the largest (32 if
+    // none). The 8B down projection (K = 12288, 256 groups) takes 192: 8 K ranges of 32
+    // workgroups walking 8 groups each, where 256 gives 6 ranges of 42 of which 4 walk
+    // 7 groups and the rest 6.
     int ks = 32;
     bool found = false;
+    long best = -1;
     const int ngrp16 = (Nv + 15) / 16;
-    for (int c : {256, 128, 64}) {
+    for (int c : {256, 192, 128, 64}) {
       if (K % (8 * c) != 0 || (p.mt > 2 && c > 128)) continue;
       const int per_range = std::max(1, num_cus() / (K / (8 * c)));  // workgroups per K range
       if (!found) { ks = c; found = true; }
-      if (ngrp16 >= 4 * per_range) { ks = c; break; }
+      if (ngrp16 >= 4 * per_range) {
+        const int wgs = std::min(per_range, ngrp16);
+        const long cost = (long)((ngrp16 + wgs - 1) / wgs) * (c + 64);
+        if (best < 0 || cost < best) { best = cost; ks = c; }
+      }
     }
     p.kchunk = 8 * ks;
     p.splits = K / p.kchunk;
@@ -1380,11 +1390,13 @@ static hipError_t launch_epi(int dtype, const GemmPlan& p, const void* X, int ld
     const int ks = p.kchunk / 8;
     if (p.mt == 1) {
       if (ks == 256) DLLM_SKINNY(1, 256);
+      else if (ks == 192) DLLM_SKINNY(1, 192);
       else if (ks == 128) DLLM_SKINNY(1, 128);
       else if (ks == 64) DLLM_SKINNY(1, 64);
       else DLLM_SKINNY(1, 32);
     } else if (p.mt == 2) {
       if (ks == 256) DLLM_SKINNY(2, 256);
+      else if (ks == 192) DLLM_SKINNY(2, 192);
       else if (ks == 128) DLLM_SKINNY(2, 128);
       else if (ks == 64) DLLM_SKINNY(2, 64);
       else DLLM_SKINNY(2, 32);
