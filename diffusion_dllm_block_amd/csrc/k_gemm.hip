@@ -1210,12 +1210,19 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
     // that give every workgroup at least 4 of the 16-column groups to walk (a workgroup
     // with fewer spends most of its time staging its activation slice and waiting for its
     // first weights: the 8B output projection, 2 groups per workgroup at 256, runs
-    // 10.3 us at 256 and 8.4 us at 128) compete on the critical path, the most groups
-    // one workgroup walks times (KS + 64) (the 64 stands for a group's fixed cost: its
-    // cross-wave sum and partial stores), larger KS on ties; else the largest (32 if
-    // none). The 8B down projection (K = 12288, 256 groups) takes 192: 8 K ranges of 32
-    // workgroups walking 8 groups each, where 256 gives 6 ranges of 42 of which 4 walk
-    // 7 groups and the rest 6.
+    // 10.3 us at 256 and 8.4 us at 128) compete on one workgroup's critical path: the
+    // most groups g it walks, plus its activation slice (as many bytes as MT groups'
+    // weights), times KS, plus 16 MT per group (a group's fixed cost: the cross-wave sum
+    // and partial stores of its MT x 16 rows); larger KS on ties; else the largest (32
+    // if none).  On the 8B cached step (same process, alternating rounds) this picks
+    // what measured fastest: the down projection (K = 12288, 256 groups) takes 192,
+    // 8 K ranges of 32 workgroups walking 8 groups each, where 256 gives 6 ranges of 42
+    // of which 4 walk 7 groups and the rest 6 (4.168 -> 4.109 ms); QKV takes 128, 12
+    // groups behind a 64 KB slice instead of 6 behind 128 KB (4.147 -> 4.121 ms);
+    // gate/up stays at 256 (128: 4.178 ms), the output projection at 128 (64: 4.185
+    // ms), the LM head at 256 (128 measured the same).  At 64 rows (prefix-mode steps)
+    // the output projection stays at 128 too (64: 935 -> 940 ms per prefix-workload
+    // generation).
     int ks = 32;
     bool found = false;
     long best = -1;
@@ -1226,7 +1233,8 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
       if (!found) { ks = c; found = true; }
       if (ngrp16 >= 4 * per_range) {
         const int wgs = std::min(per_range, ngrp16);
-        const long cost = (long)((ngrp16 + wgs - 1) / wgs) * (c + 64);
+        const long g = (ngrp16 + wgs - 1) / wgs;
+        const long cost = (g + p.mt) * c + 16L * p.mt * g;
         if (best < 0 || cost < best) { best = cost; ks = c; }
       }
     }
