@@ -164,10 +164,9 @@ __device__ __forceinline__ void consume_subtile(const KVTile16& t, int key0,
   }
 }
 
-// ONE: every wave has a single 32-key sub-tile (nsub == 1): one operand tile in
-// registers, so two workgroups fit on a CU.
-template <int NW, bool ONE>
-__global__ __launch_bounds__(NW * 64, ONE ? 2 : 1) void attn_splitkv_bf16(
+// Plans with a single sub-tile per wave run attn_splitkv_ds_bf16 below instead.
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_splitkv_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
     int Sp, int nqt, int nchunk, int nsub, float scale_log2, float* __restrict__ part) {
@@ -226,9 +225,7 @@ __global__ __launch_bounds__(NW * 64, ONE ? 2 : 1) void attn_splitkv_bf16(
     consume_subtile(t, key0, qf, oacc, m_run, l_run, S, scale_log2, j);
   };
 
-  if constexpr (ONE) {
-    consume(ta, wkey0);
-  } else {
+  {
     // The next sub-tile is always requested, past the end too (clamped addresses, never
     // consumed): with no load under a branch, the wait before each consume counts only
     // the sub-tile it needs, and the following one stays in flight.
@@ -339,6 +336,186 @@ __global__ __launch_bounds__(NW * 64, ONE ? 2 : 1) void attn_splitkv_bf16(
     if (d4 == 0) {
       pc[32 * HD + qi] = Mq[it];
       pc[32 * HD + 32 + qi] = Lq[it];
+    }
+  }
+}
+
+// ============================================================================
+// Split-KV attention with one 32-key sub-tile per wave and the P.V product split over the
+// head dim: grid (nchunk, Hq*nqt, B), NW waves, chunks of NW*32 keys, 32 query rows.
+// Wave w scores sub-tile w (S^T = K . Q^T as in attn_splitkv_bf16); the waves exchange
+// their row maxima, so every P is taken against the chunk maximum M, and hand P over
+// through LDS as bf16 (2 KB per wave); wave w then forms O^T for dims
+// [16 DT w, 16 DT (w + 1)) over all NW sub-tiles (DT = 8 / NW 16-dim tiles), reading
+// those dims' Vt rows of the whole chunk (1 KB contiguous per sub-tile and 16-dim tile).
+// No wave holds a whole 32 x 128 O tile, so no fp32 O goes through LDS: the chunk
+// result (O, M, l), or with a single chunk the normalised output, leaves straight from
+// each wave's accumulators.  Same products and MFMA count as the per-wave online form.
+// ============================================================================
+template <int NW>
+__global__ __launch_bounds__(NW * 64, 2) void attn_splitkv_ds_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
+    int Sp, int nqt, int nchunk, float scale_log2, float* __restrict__ part) {
+  constexpr int NT = NW * 64, DT = 8 / NW;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  __shared__ float red_m[NW][32], red_l[NW][32];
+  __shared__ __attribute__((aligned(16))) uint16_t qs[32 * QS_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t ps[NW][32][32];  // P [sub-tile][query][key]
+  const int chunk = blockIdx.x;
+  const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
+  const int hkv = hq / (Hq / Hkv);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, j = l >> 4;
+  const int ckey0 = chunk * NW * 32;  // the chunk's first key
+  const int wkey0 = ckey0 + 32 * w;   // this wave's score sub-tile
+
+  // Q tile: read once per workgroup, staged in LDS (rows >= R clamped: never stored)
+  constexpr int QP = 512 / NT;
+  const uint16_t* qh = q + ((int64_t)b * Hq + hq) * R * HD;
+  u32x4 qg[QP];
+#pragma unroll
+  for (int u = 0; u < QP; ++u) {
+    const int e = threadIdx.x + NT * u;
+    qg[u] = *reinterpret_cast<const u32x4*>(qh + (int64_t)min(qt * 32 + (e >> 4), R - 1) * HD +
+                                            8 * (e & 15));
+  }
+  const uint16_t* kbase = k + ((int64_t)b * Hkv + hkv) * Sp * HD;
+  const uint16_t* vbase = vt + ((int64_t)b * Hkv + hkv) * HD * Sp;
+  // K rows of the wave's sub-tile, in the score-row order of attn_splitkv_bf16 (keys >= S
+  // read key S - 1: their scores are masked)
+  u32x4 kk[2][4];
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) {
+    const int key = min(wkey0 + 8 * (li >> 2) + 4 * tau + (li & 3), S - 1);
+    const uint16_t* kp = kbase + (int64_t)key * HD + 8 * j;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) kk[tau][st] = *reinterpret_cast<const u32x4*>(kp + 32 * st);
+  }
+  // Vt rows of the wave's dims for every sub-tile: dim 16 (DT w + dt) + li, keys
+  // 32 s + 8j .. +8 of the chunk (masked where used, on sub-tiles that reach S)
+  u32x4 vv[NW][DT];
+#pragma unroll
+  for (int s = 0; s < NW; ++s)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vv[s][dt] = load8_raw(vbase, 16 * (DT * w + dt) + li, ckey0 + 32 * s + 8 * j, Sp);
+#pragma unroll
+  for (int u = 0; u < QP; ++u) {
+    const int e = threadIdx.x + NT * u;
+    *reinterpret_cast<u32x4*>(&qs[(e >> 4) * QS_LD + 8 * (e & 15)]) = qg[u];
+  }
+  __syncthreads();
+
+  // scores of the wave's 32 keys for both 16-query tiles: lane holds keys wkey0 + 8j + e
+  float p[2][8];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    u32x4 qf[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      qf[st] = *reinterpret_cast<const u32x4*>(&qs[(16 * qq + li) * QS_LD + 8 * j + 32 * st]);
+    f32x4 sc[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau) {
+      sc[tau] = f32x4{};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        sc[tau] = mfma16(as_bf16x8(kk[tau][st]), as_bf16x8(qf[st]), sc[tau]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (wkey0 + 8 * j + e < S) ? sc[e >> 2][e & 3] * scale_log2 : -INFINITY;
+      p[qq][e] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = xor32_combine(xor16_combine(mx, fmax_op), fmax_op);
+    if (j == 0) red_m[w][16 * qq + li] = mx;
+  }
+  __syncthreads();
+  // P against the chunk maximum (a row with no valid key in the chunk gets P = 0, l = 0)
+  float M[2];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qi = 16 * qq + li;
+    float m = red_m[0][qi];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) m = fmaxf(m, red_m[i][qi]);
+    M[qq] = m;
+    float ls = 0.f;
+    u16x8 pb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(p[qq][e] - m);
+      ls += x;
+      pb[e] = f2bf(x);
+    }
+    ls = xor32_combine(xor16_combine(ls, add_op), add_op);
+    if (j == 0) red_l[w][qi] = ls;
+    *reinterpret_cast<u16x8*>(&ps[w][qi][8 * j]) = pb;
+  }
+  __syncthreads();
+
+  // O^T (dims x queries) += Vt . P^T over the chunk's sub-tiles
+  f32x4 oacc[2][DT];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[qq][dt] = f32x4{};
+#pragma unroll
+  for (int s = 0; s < NW; ++s) {
+    const int key0 = ckey0 + 32 * s;
+    const bool tail = key0 + 32 > S;  // uniform over the workgroup
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const bf16x8 pop = as_bf16x8(*reinterpret_cast<const u32x4*>(&ps[s][16 * qq + li][8 * j]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 va = tail ? mask8(vv[s][dt], S - (key0 + 8 * j)) : vv[s][dt];
+        oacc[qq][dt] = mfma16(as_bf16x8(va), pop, oacc[qq][dt]);
+      }
+    }
+  }
+  // lane holds dims 16 (DT w + dt) + 4j + r of query 16 qq + li
+  float L[2];
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) s += red_l[i][16 * qq + li];
+    L[qq] = s;
+  }
+  if (nchunk == 1) {
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      const int row = qt * 32 + 16 * qq + li;
+      if (row < R) {
+        const float inv = 1.0f / L[qq];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const f32x4 a = oacc[qq][dt];
+          *reinterpret_cast<u16x4*>(o + ((int64_t)b * R + row) * (Hq * HD) + hq * HD +
+                                    16 * (DT * w + dt) + 4 * j) =
+              u16x4{f2bf(a[0] * inv), f2bf(a[1] * inv), f2bf(a[2] * inv), f2bf(a[3] * inv)};
+        }
+      }
+    }
+    return;
+  }
+  const int64_t grp = ((int64_t)b * Hq + hq) * nqt + qt;
+  float* pc = part + (grp * nchunk + chunk) * kPartStride;
+#pragma unroll
+  for (int qq = 0; qq < 2; ++qq) {
+    const int qi = 16 * qq + li;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const f32x4 a = oacc[qq][dt];
+      *reinterpret_cast<float4*>(pc + qi * HD + 16 * (DT * w + dt) + 4 * j) =
+          make_float4(a[0], a[1], a[2], a[3]);
+    }
+    if (w == 0 && j == 0) {
+      pc[32 * HD + qi] = M[qq];
+      pc[32 * HD + 32 + qi] = L[qq];
     }
   }
 }
@@ -731,6 +908,8 @@ constexpr int kMaxChunks = 64;
 // Step attention (at most 256 query rows: a block step, or the block and suffix rows of a
 // prefix-mode step, where the 128-row flash tiles would give only 32-64 workgroups; prefix
 // workload 926 -> 920 ms per generation), 32-row query tiles, 32-key sub-tiles per wave:
+// (plans with one sub-tile per wave run attn_splitkv_ds_bf16: 8B cached step 4.159 ->
+// 4.090 ms against the per-wave online form with an LDS merge of the waves' O tiles):
 //  * one sub-tile per wave in eight-wave workgroups (256-key chunks: half the partials
 //    to merge of four-wave chunks) when that gives 160 to 1024 workgroups (32 query rows
 //    x 32 heads against 1032-1500 keys, kernel-only: 14.4-15.7 us with 9-12 four-wave
@@ -811,15 +990,20 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
   if (p.kind == 1) {
     if (p.nchunk > 1 && !part) return hipErrorInvalidValue;
     const dim3 grid(p.nchunk, Hq * p.nqt, B);
-#define DLLM_ATTN(NWV, ONEV)                                                                  \
-  attn_splitkv_bf16<NWV, ONEV><<<grid, NWV * 64, 0, st>>>(                                    \
+#define DLLM_ATTN(NWV)                                                                        \
+  attn_splitkv_bf16<NWV><<<grid, NWV * 64, 0, st>>>(                                          \
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, S, \
       Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part)
-    if (p.nw == 8 && p.nsub == 1) DLLM_ATTN(8, true);
-    else if (p.nw == 4 && p.nsub == 1) DLLM_ATTN(4, true);
-    else if (p.nw == 4) DLLM_ATTN(4, false);
+#define DLLM_ATTN_DS(NWV)                                                                     \
+  attn_splitkv_ds_bf16<NWV><<<grid, NWV * 64, 0, st>>>(                                       \
+      (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, S, \
+      Sp, p.nqt, p.nchunk, scale_log2, part)
+    if (p.nw == 8 && p.nsub == 1) DLLM_ATTN_DS(8);
+    else if (p.nw == 4 && p.nsub == 1) DLLM_ATTN_DS(4);
+    else if (p.nw == 4) DLLM_ATTN(4);
     else return hipErrorInvalidValue;  // the plan never asks for 8 waves x several sub-tiles
 #undef DLLM_ATTN
+#undef DLLM_ATTN_DS
     if (p.nchunk > 1) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
