@@ -103,9 +103,18 @@ __device__ __forceinline__ void load_kv16(KVTile16& t, const uint16_t* kbase,
   for (int dt = 0; dt < 8; ++dt) t.v[dt] = load8_raw(vbase, 16 * dt + li, key0 + 8 * j, Sp);
 }
 
-// Chunk partial of one group: O [32][HD] unnormalised (scaled to the chunk maximum m),
-// then m [32] and l [32].
-constexpr int kPartStride = 32 * HD + 64;
+// Chunk partial of one group: O [32][HD] unnormalised (scaled to the chunk maximum m) in
+// bf16, then m [32] and l [32] in fp32: kPartStride floats per (group, chunk), m at float
+// kPartML.  The bf16 O halves the bytes the chunk kernels write and attn_combine reads
+// back (relative rounding 2^-9 per partial, as for the bf16 output itself).
+constexpr int kPartML = 32 * HD / 2;
+constexpr int kPartStride = kPartML + 64;
+
+__device__ __forceinline__ void part_store_o(float* pc, int qi, int d, float a0, float a1,
+                                             float a2, float a3) {
+  *reinterpret_cast<u16x4*>(reinterpret_cast<uint16_t*>(pc) + qi * HD + d) =
+      u16x4{f2bf(a0), f2bf(a1), f2bf(a2), f2bf(a3)};
+}
 
 // The products of one 32-key sub-tile (keys key0 ..) for 32 query rows (two 16-row tiles;
 // lane (l%16, j = l/16)), folded into the rows' online-softmax state (O^T unnormalised,
@@ -332,10 +341,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_splitkv_bf16(
   for (int it = 0; it < PAIRS; ++it) {
     const int e = threadIdx.x + NT * it;
     const int qi = e >> 5, d4 = (e & 31) * 4;
-    *reinterpret_cast<float4*>(pc + qi * HD + d4) = acc[it];
+    part_store_o(pc, qi, d4, acc[it].x, acc[it].y, acc[it].z, acc[it].w);
     if (d4 == 0) {
-      pc[32 * HD + qi] = Mq[it];
-      pc[32 * HD + 32 + qi] = Lq[it];
+      pc[kPartML + qi] = Mq[it];
+      pc[kPartML + 32 + qi] = Lq[it];
     }
   }
 }
@@ -510,12 +519,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_splitkv_ds_bf16(
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const f32x4 a = oacc[qq][dt];
-      *reinterpret_cast<float4*>(pc + qi * HD + 16 * (DT * w + dt) + 4 * j) =
-          make_float4(a[0], a[1], a[2], a[3]);
+      part_store_o(pc, qi, 16 * (DT * w + dt) + 4 * j, a[0], a[1], a[2], a[3]);
     }
     if (w == 0 && j == 0) {
-      pc[32 * HD + qi] = M[qq];
-      pc[32 * HD + 32 + qi] = L[qq];
+      pc[kPartML + qi] = M[qq];
+      pc[kPartML + 32 + qi] = L[qq];
     }
   }
 }
@@ -639,11 +647,11 @@ __global__ __launch_bounds__(512, 1) void attn_gqa_bf16(
     const int qi = 16 * qq + li;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      *reinterpret_cast<float4*>(pcb + qi * HD + 16 * dt + 4 * j) =
-          make_float4(oacc[qq][dt][0], oacc[qq][dt][1], oacc[qq][dt][2], oacc[qq][dt][3]);
+      part_store_o(pcb, qi, 16 * dt + 4 * j, oacc[qq][dt][0], oacc[qq][dt][1],
+                   oacc[qq][dt][2], oacc[qq][dt][3]);
     if (j == 0) {
-      pcb[32 * HD + qi] = m_run[qq];
-      pcb[32 * HD + 32 + qi] = l_run[qq];
+      pcb[kPartML + qi] = m_run[qq];
+      pcb[kPartML + 32 + qi] = l_run[qq];
     }
   }
 }
@@ -673,9 +681,11 @@ __global__ __launch_bounds__(128) void attn_combine(const float* __restrict__ pa
     for (int u = 0; u < 16; ++u) {
       const int c = min(c0 + u, nchunk - 1);  // clamped; chunks past nchunk are dropped
       const float* pc = pg + (int64_t)c * kPartStride;
-      mc[u] = pc[32 * HD + qi];
-      lc[u] = pc[32 * HD + 32 + qi];
-      v[u] = *reinterpret_cast<const float4*>(pc + qi * HD + d4);
+      mc[u] = pc[kPartML + qi];
+      lc[u] = pc[kPartML + 32 + qi];
+      const u16x4 r = *reinterpret_cast<const u16x4*>(reinterpret_cast<const uint16_t*>(pc) +
+                                                      qi * HD + d4);
+      v[u] = make_float4(bf2f(r[0]), bf2f(r[1]), bf2f(r[2]), bf2f(r[3]));
     }
     // online merge in chunk order (the same result as rescaling by the global max)
 #pragma unroll
