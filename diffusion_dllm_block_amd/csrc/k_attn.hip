@@ -546,11 +546,16 @@ constexpr int GQ_MAXSUB = 8;        // at most 256 keys per chunk (128 KB of LDS
 
 __device__ __forceinline__ int gq_kswz(int r) { return (r & 3) | ((r >> 3) << 2); }
 
+// NSUB: the chunk's 32-key sub-tiles, a compile-time count so that the walk over a full
+// chunk is unrolled and the scheduler can start a sub-tile's operand reads and score
+// products while the previous one is in its softmax.
+template <int NSUB>
 __global__ __launch_bounds__(512, 1) void attn_gqa_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, uint16_t* __restrict__ o, int Hq, int Hkv, int R, int S,
-    int Sp, int nchunk, int ck, float scale_log2, float* __restrict__ part) {
+    int Sp, int nchunk, float scale_log2, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
+  constexpr int ck = 32 * NSUB;
   const int chunk = blockIdx.x, b = blockIdx.y / Hkv, hkv = blockIdx.y % Hkv;
   const int G = Hq / Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(512, 1) void attn_gqa_bf16(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[qq][dt] = f32x4{};
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-  for (int sub = 0; sub < nsub; ++sub) {
+  auto walk = [&](int sub) {
     const unsigned char* base = gsm + sub * GQ_SUB;
     KVTile16 t;
 #pragma unroll
@@ -621,6 +626,13 @@ __global__ __launch_bounds__(512, 1) void attn_gqa_bf16(
       t.v[dt] = *reinterpret_cast<const u32x4*>(base + 8192 + d * 64 + ((j ^ ((d >> 2) & 3)) * 16));
     }
     consume_subtile(t, key_lo + 32 * sub, qf, oacc, m_run, l_run, S, scale_log2, j);
+  };
+  if (NSUB <= 4 && nsub == NSUB) {  // a full chunk (all but a ragged last one); longer
+                                    // unrolled walks spill
+#pragma unroll
+    for (int sub = 0; sub < NSUB; ++sub) walk(sub);
+  } else {
+    for (int sub = 0; sub < nsub; ++sub) walk(sub);
   }
 
   // lane holds query 16 qq + li, dims 16 dt + 4j .. +4
@@ -1022,17 +1034,33 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
     }
   } else if (p.kind == 3) {
     if (p.nchunk > 1 && !part) return hipErrorInvalidValue;
-    static bool attr_set = false;  // opt in to more than 64 KB of dynamic LDS once
-    if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_gqa_bf16),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           GQ_MAXSUB * GQ_SUB);
-      if (err != hipSuccess) return err;
-      attr_set = true;
+    static bool attr_set[GQ_MAXSUB + 1] = {};  // opt in to > 64 KB of dynamic LDS once each
+    const int nsubk = p.ck / 32;
+    if (p.ck % 32 != 0 || nsubk < 1 || nsubk > GQ_MAXSUB) return hipErrorInvalidValue;
+#define DLLM_GQA(NS)                                                                          \
+  do {                                                                                        \
+    if (!attr_set[NS]) {                                                                      \
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_gqa_bf16<NS>), \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,        \
+                                           NS * GQ_SUB);                                      \
+      if (err != hipSuccess) return err;                                                      \
+      attr_set[NS] = true;                                                                    \
+    }                                                                                         \
+    attn_gqa_bf16<NS><<<dim3(p.nchunk, B * Hkv), 512, NS * GQ_SUB, st>>>(                     \
+        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, \
+        S, Sp, p.nchunk, scale_log2, part);                                                   \
+  } while (0)
+    switch (nsubk) {
+      case 1: DLLM_GQA(1); break;
+      case 2: DLLM_GQA(2); break;
+      case 3: DLLM_GQA(3); break;
+      case 4: DLLM_GQA(4); break;
+      case 5: DLLM_GQA(5); break;
+      case 6: DLLM_GQA(6); break;
+      case 7: DLLM_GQA(7); break;
+      default: DLLM_GQA(8); break;
     }
-    attn_gqa_bf16<<<dim3(p.nchunk, B * Hkv), 512, (p.ck / 32) * GQ_SUB, st>>>(
-        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R,
-        S, Sp, p.nchunk, p.ck, scale_log2, part);
+#undef DLLM_GQA
     if (p.nchunk > 1) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
