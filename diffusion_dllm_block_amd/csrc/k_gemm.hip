@@ -335,18 +335,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   };
   u32x4 wr[C::NLOAD];
   {
-    // activation slice -> LDS (rows >= M read row M-1; their outputs are never used).
-    // The first group's weight loads are issued between the activation loads and their
-    // LDS stores: the stores then wait only for the activation loads (issued first), and
-    // the weight stream's first HBM round trip overlaps the staging instead of following
-    // it.  The weight loads go in t order, like the refills in the loop, so that the
-    // loop's wait counts are the same on entry and on the back edge.
-    u32x4 xr[C::XV];
+    // activation slice -> LDS by direct global->LDS loads (rows >= M read row M-1; their
+    // outputs are never used).  Load slot s fills LDS bytes [1024 s, 1024 s + 1024) of
+    // the padded slice, lane l its 16-byte chunk q = 64 s + l: row q / RC, chunk q % RC
+    // of that row, where chunk RC - 1 is the row's pad (it loads an in-row chunk, never
+    // read).  The first group's weight loads follow in t order, like the refills in the
+    // loop, and the wait before the barrier leaves just them in flight, so the weight
+    // stream's first HBM round trip overlaps the staging and the loop's wait counts are
+    // the same on entry and on the back edge.
+    constexpr int RC = C::LDX / 8;            // 16-byte chunks per LDS row, pad included
+    constexpr int NCH = MT * 16 * RC;         // chunks in the slice
+    constexpr int NSLOT = (NCH + 63) / 64;    // 1 KB load slots
+    unsigned char* xsb = reinterpret_cast<unsigned char*>(Xs);
 #pragma unroll
-    for (int i = 0; i < C::XV; ++i) {
-      const int ee = tid + 512 * i;
-      const int r = ee / (C::KW / 8), c8 = ee % (C::KW / 8);
-      xr[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)min(r, M - 1) * ldx + kw0 + 8 * c8);
+    for (int it = 0; it < (NSLOT + 7) / 8; ++it) {
+      const int slot = it * 8 + w;
+      if (slot < NSLOT) {  // uniform over the wave
+        const int q = slot * 64 + l;
+        const int r = q / RC, cc = q % RC;
+        const uint16_t* src =
+            X + (int64_t)min(r, M - 1) * ldx + kw0 + 8 * min(cc, RC - 2);
+        if (q < NCH)
+          __builtin_amdgcn_global_load_lds(
+              (const __attribute__((address_space(1))) void*)src,
+              (__attribute__((address_space(3))) void*)(xsb + slot * 1024), 16, 0, 0);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* wp = wptr(min(wid, ngrp - 1));
@@ -355,12 +368,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       wr[t] = *reinterpret_cast<const u32x4*>(wp + 32 * t);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int i = 0; i < C::XV; ++i) {
-      const int ee = tid + 512 * i;
-      const int r = ee / (C::KW / 8), c8 = ee % (C::KW / 8);
-      *reinterpret_cast<u32x4*>(&Xs[r * C::LDX + 8 * c8]) = xr[i];
-    }
+    // this wave's slice loads have landed once only the NLOAD weight loads are in flight
+    __builtin_amdgcn_s_waitcnt((C::NLOAD & 15) | ((C::NLOAD >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
   }
   __syncthreads();
 
