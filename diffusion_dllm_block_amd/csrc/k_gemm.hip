@@ -304,13 +304,11 @@ template <int MT, int KS> struct SkinnyCfg {
   static constexpr int KW = 8 * KS;                  // K range of a workgroup
   static constexpr int NLOAD = KS / 32;              // weight loads per lane per group
   static constexpr int LDX = KW + 8;                 // LDS row stride (elements)
-  static constexpr int XV = MT * 16 * KW / 8 / 512;  // 16-byte activation loads per thread
   static constexpr int SLOTS = MT * 4;               // result rows of 64 lanes per group
   // the cross-wave sums go through LDS at most 8 result rows at a time, which leaves
   // room for a 128-deep per-wave K range at 64 rows (64 x 24576 x 4096: 67.8 -> 48.6 us
   // against a 64-deep one, whose 2 loads per lane in flight starved the weight stream)
   static constexpr int RS = SLOTS < 8 ? SLOTS : 8;
-  static_assert(XV >= 1, "activation slice smaller than one load per thread");
   static_assert(MT * 16 * LDX * 2 + 8 * RS * 64 * 4 <= 160 * 1024, "LDS budget");
 };
 
