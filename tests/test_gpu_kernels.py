@@ -209,6 +209,12 @@ ATTN_CASES = [
     ("two_row_tiles", 1, 2, 1, 64, 300, "bf16"),
     # 200 query rows: seven 32-row query tiles on the split-KV kernel (prefix-mode steps)
     ("split_kv_200_rows", 1, 2, 2, 200, 333, "bf16"),
+    # the prefix workload's first step: 256 query rows (eight 32-row tiles) against 512
+    # keys, eight-wave chunks of 256 keys with the P.V product split over the head dim
+    ("prefix_256_rows_kv512", 1, 32, 32, 256, 512, "bf16"),
+    # grouped query heads, chunks of four sub-tiles (walked unrolled) and a last chunk of
+    # four keys (one sub-tile, walked by the loop)
+    ("gqa_7to1_b8_ragged_last", 8, 28, 4, 32, 900, "bf16"),
     # past 256 rows the flash kernel: three 128-row tiles, the last ragged
     ("flash_300_rows", 1, 2, 2, 300, 333, "bf16"),
     ("flash_refresh_shape", 1, 4, 4, 2024, 2024, "bf16"),
