@@ -206,6 +206,9 @@ ATTN_CASES = [
     # 17 eight-wave chunks: the merge walks its chunks in three rounds of loads
     ("many_chunks_ragged", 1, 32, 32, 32, 4100, "bf16"),
     ("ragged_rows_keys", 1, 4, 2, 20, 77, "bf16"),
+    # one KV head per query head with 20 query rows: the head-dim-split kernel with 12
+    # clamped rows, four-wave chunks of 128 keys, the last one 104 keys
+    ("mha_rows20_ragged", 1, 8, 8, 20, 1000, "bf16"),
     ("two_row_tiles", 1, 2, 1, 64, 300, "bf16"),
     # 200 query rows: seven 32-row query tiles on the split-KV kernel (prefix-mode steps)
     ("split_kv_200_rows", 1, 2, 2, 200, 333, "bf16"),
@@ -267,9 +270,13 @@ GEMM_CASES = [
     ("skinny_m7_ragged_n", 7, 1000, 512, "bf16"),
     ("skinny_m50_two_tiles", 50, 384, 1024, "bf16"),
     ("skinny_m32_down_k12288", 32, 512, 12288, "bf16"),
-    # the 8B down projection (6 K ranges of 2048 over 42-43 workgroups each), 16 rows too
+    # the 8B down projection (8 K ranges of 1536, 192-deep per wave, over 32 workgroups
+    # each), 16 rows too
     ("skinny_m32_down_full", 32, 4096, 12288, "bf16"),
     ("skinny_m16_down_full", 16, 4096, 12288, "bf16"),
+    # 33 rows: four 16-row MFMA tiles, 31 of the 64 staged rows clamped to the last; the
+    # staged slice (64 rows of 1024 columns plus a pad chunk) ends in a partial load slot
+    ("skinny_m33_clamped_rows", 33, 1024, 2048, "bf16"),
     ("tiled_m300_ragged", 300, 384, 512, "bf16"),
     # mid (64 < M <= 256): every tile split over K / whole tiles plus a split ragged
     # last round (2 rounds of 256 whole tiles, 9 tail tiles in 4 K pieces) / ragged N
