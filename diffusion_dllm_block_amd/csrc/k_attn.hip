@@ -60,7 +60,7 @@ __device__ __forceinline__ u32x4 mask8(const u32x4& v, int n) {
 }
 
 // ============================================================================
-// Split-KV attention for a few query rows (a block step): grid (nchunk, Hq*nqt, B),
+// Split-KV attention for a few query rows (a block step): grid (Hq*nqt, nchunk, B),
 // NW waves (4 or 8), 32 query rows per workgroup.  Chunk c covers keys
 // [c*NW*kpw, (c+1)*NW*kpw); wave w walks its kpw keys in 32-key sub-tiles with an online
 // softmax, loading the next sub-tile while the current one is in the MFMAs.
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_splitkv_bf16(
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ float red_m[NW][32], red_l[NW][32];
   __shared__ __attribute__((aligned(16))) float osum[NH][32][SK_OLD];
-  const int chunk = blockIdx.x;
-  const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
+  const int chunk = blockIdx.y;
+  const int hq = blockIdx.x / nqt, qt = blockIdx.x % nqt, b = blockIdx.z;
   const int hkv = hq / (Hq / Hkv);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, j = l >> 4;
   const int kpw = 32 * nsub;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_splitkv_bf16(
 
 // ============================================================================
 // Split-KV attention with one 32-key sub-tile per wave and the P.V product split over the
-// head dim: grid (nchunk, Hq*nqt, B), NW waves, chunks of NW*32 keys, 32 query rows.
+// head dim: grid (Hq*nqt, nchunk, B), NW waves, chunks of NW*32 keys, 32 query rows.
 // Wave w scores sub-tile w (S^T = K . Q^T as in attn_splitkv_bf16); the waves exchange
 // their row maxima, so every P is taken against the chunk maximum M, and hand P over
 // through LDS as bf16 (2 KB per wave); wave w then forms O^T for dims
@@ -371,8 +371,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_splitkv_ds_bf16(
   __shared__ float red_m[NW][32], red_l[NW][32];
   __shared__ __attribute__((aligned(16))) uint16_t qs[32 * QS_LD];
   __shared__ __attribute__((aligned(16))) uint16_t ps[NW][32][32];  // P [sub-tile][query][key]
-  const int chunk = blockIdx.x;
-  const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
+  const int chunk = blockIdx.y;
+  const int hq = blockIdx.x / nqt, qt = blockIdx.x % nqt, b = blockIdx.z;
   const int hkv = hq / (Hq / Hkv);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, j = l >> 4;
   const int ckey0 = chunk * NW * 32;  // the chunk's first key
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_splitkv_ds_bf16(
 
 // ============================================================================
 // Grouped-query step attention (G = Hq / Hkv query heads per KV head, 2 <= G <= 8, at
-// most 32 query rows): grid (nchunk, B * Hkv), 8 waves.  Wave w < G takes query head
+// most 32 query rows): grid (B * Hkv, nchunk), 8 waves.  Wave w < G takes query head
 // hkv * G + w through every 32-key sub-tile of the chunk; the chunk's K and Vt are read
 // from memory once per KV head into LDS (direct global->LDS loads) instead of once per
 // query head, and each wave reads them from there in the split-KV kernel's operand
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(512, 1) void attn_gqa_bf16(
     int Sp, int nchunk, float scale_log2, float* __restrict__ part) {
   extern __shared__ __attribute__((aligned(16))) unsigned char gsm[];
   constexpr int ck = 32 * NSUB;
-  const int chunk = blockIdx.x, b = blockIdx.y / Hkv, hkv = blockIdx.y % Hkv;
+  const int chunk = blockIdx.y, b = blockIdx.x / Hkv, hkv = blockIdx.x % Hkv;
   const int G = Hq / Hkv;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & 63, li = l & 15, j = l >> 4;
@@ -1011,7 +1011,11 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
   const float scale_log2 = kLog2e / sqrtf((float)D);
   if (p.kind == 1) {
     if (p.nchunk > 1 && !part) return hipErrorInvalidValue;
-    const dim3 grid(p.nchunk, Hq * p.nqt, B);
+    // head-major: workgroup ids run over (head, query tile) first, so with Hq * nqt a
+    // multiple of 8 every chunk of one head lands on one XCD and the head's Q tile is read
+    // from memory once per XCD rather than once per chunk (8B cached step 4.085 -> 4.064
+    // ms, bit-identical)
+    const dim3 grid(Hq * p.nqt, p.nchunk, B);
 #define DLLM_ATTN(NWV)                                                                        \
   attn_splitkv_bf16<NWV><<<grid, NWV * 64, 0, st>>>(                                          \
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, S, \
@@ -1046,7 +1050,7 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
       if (err != hipSuccess) return err;                                                      \
       attr_set[NS] = true;                                                                    \
     }                                                                                         \
-    attn_gqa_bf16<NS><<<dim3(p.nchunk, B * Hkv), 512, NS * GQ_SUB, st>>>(                     \
+    attn_gqa_bf16<NS><<<dim3(B * Hkv, p.nchunk), 512, NS * GQ_SUB, st>>>(                     \
         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, \
         S, Sp, p.nchunk, scale_log2, part);                                                   \
   } while (0)
