@@ -60,7 +60,7 @@ __device__ __forceinline__ u32x4 mask8(const u32x4& v, int n) {
 }
 
 // ============================================================================
-// Split-KV attention for a few query rows (a block step): grid (Hq*nqt, nchunk, B),
+// Split-KV attention for a few query rows (a block step): grid (nchunk, Hq*nqt, B),
 // NW waves (4 or 8), 32 query rows per workgroup.  Chunk c covers keys
 // [c*NW*kpw, (c+1)*NW*kpw); wave w walks its kpw keys in 32-key sub-tiles with an online
 // softmax, loading the next sub-tile while the current one is in the MFMAs.
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_splitkv_bf16(
   static_assert(NW == 4 || NW == 8, "four or eight waves");
   __shared__ float red_m[NW][32], red_l[NW][32];
   __shared__ __attribute__((aligned(16))) float osum[NH][32][SK_OLD];
-  const int chunk = blockIdx.y;
-  const int hq = blockIdx.x / nqt, qt = blockIdx.x % nqt, b = blockIdx.z;
+  const int chunk = blockIdx.x;
+  const int hq = blockIdx.y / nqt, qt = blockIdx.y % nqt, b = blockIdx.z;
   const int hkv = hq / (Hq / Hkv);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, li = l & 15, j = l >> 4;
   const int kpw = 32 * nsub;
@@ -1011,13 +1011,15 @@ hipError_t launch_attention(int dtype, const AttnPlan& p, const void* q, const v
   const float scale_log2 = kLog2e / sqrtf((float)D);
   if (p.kind == 1) {
     if (p.nchunk > 1 && !part) return hipErrorInvalidValue;
-    // head-major: workgroup ids run over (head, query tile) first, so with Hq * nqt a
-    // multiple of 8 every chunk of one head lands on one XCD and the head's Q tile is read
-    // from memory once per XCD rather than once per chunk (8B cached step 4.085 -> 4.064
-    // ms, bit-identical)
+    // one sub-tile per wave: head-major, workgroup ids running over (head, query tile)
+    // first, so with Hq * nqt a multiple of 8 every chunk of one head lands on one XCD
+    // and the head's Q tile is read from memory once per XCD rather than once per chunk
+    // (8B cached step 4.085 -> 4.064 ms, bit-identical); several sub-tiles per wave (long
+    // key ranges, where the Q tile is a small share of a chunk's bytes): chunk-major
+    // (16384 keys kernel-only 60.5 -> 59.6 us against head-major)
     const dim3 grid(Hq * p.nqt, p.nchunk, B);
 #define DLLM_ATTN(NWV)                                                                        \
-  attn_splitkv_bf16<NWV><<<grid, NWV * 64, 0, st>>>(                                          \
+  attn_splitkv_bf16<NWV><<<dim3(p.nchunk, Hq * p.nqt, B), NWV * 64, 0, st>>>(                 \
       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)vt, (uint16_t*)o, Hq, Hkv, R, S, \
       Sp, p.nqt, p.nchunk, p.nsub, scale_log2, part)
 #define DLLM_ATTN_DS(NWV)                                                                     \
