@@ -249,3 +249,49 @@ def test_prefix_mode_with_empty_prompt_is_the_full_forward_at_every_step():
         else:
             assert dual_err > 1e-3, f"step {n}: DualCache should read a stale suffix"
     assert n == 4
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (4, 2)])
+def test_dualcache_is_exact_when_only_one_layer_mixes_positions(Hq, Hkv):
+    """DualCache keeps every position outside the block at the K/V of the last refresh
+    and recomputes only the block rows (ccyt168.com Fast-dLLM article, section 1.1;
+    techwalker.com explainer, "Core innovation").  The cached values go stale only
+    because attention mixes positions: with the output projection of every layer but
+    one (l*) set to zero, the inputs of layers 0..l* depend on each position's own token
+    alone, so the K/V cached at layer l* equal fresh ones at every unchanged position,
+    and the layers after l* (zero output projection) never use their cached K/V.  Every
+    DualCache step of every block, later steps included, must then equal the no-cache
+    full forward of the current tokens.  This pins the layer-l* cache read of the step
+    for each l*: a step that skipped the masked suffix, kept the block's stale K/V, read
+    another layer's cache or put the block at the wrong RoPE positions fails it.  With
+    every projection kept, the steps after the first do differ (the stale cache)."""
+    wl = replace(small_workload("f32", Hq, Hkv), prompt_len=5, gen_len=12, block_len=4)
+    wl = replace(wl, model=replace(wl.model, n_layers=3))
+    base = synth.make_weights(wl)
+    prompt = synth.make_prompt(wl)
+    L = wl.model.n_layers
+    for l_star in list(range(L)) + [None]:
+        W = dict(base)
+        if l_star is not None:
+            for l in range(L):
+                if l != l_star:
+                    W[f"w_o.{l}"] = np.zeros_like(base[f"w_o.{l}"])
+        M = om.OracleModel(wl, weights=W)
+        s = Session(M, prompt, wl.gen_len, wl.block_len, 1.5, "dual")  # one token per step
+        worst_later = 0.0
+        for b in range(wl.gen_len // wl.block_len):
+            s.refresh()
+            s0, s1 = s.block_span(b)
+            n = 0
+            while not s.block_done(b):
+                n += 1
+                _, ref = om.full_forward(M, s.tokens, logit_rows=slice(s0, s1))
+                out = s.step(b)
+                err = np.max(np.abs(out["logits"] - ref))
+                if l_star is not None or n == 1:
+                    assert err < 1e-11, f"l*={l_star} block {b} step {n}: {err}"
+                else:
+                    worst_later = max(worst_later, err)
+            assert n == wl.block_len
+        if l_star is None:
+            assert worst_later > 1e-3, "the stale cache should show with every layer mixing"
