@@ -599,6 +599,47 @@ def test_prefix_mode_empty_prompt_every_step_equals_full_forward(lib):
     assert n == wl.block_len
 
 
+@pytest.mark.parametrize("l_star,Hkv", [(0, 4), (1, 4), (1, 2)])
+def test_dualcache_one_mixing_layer_every_step_equals_full_forward(lib, l_star, Hkv):
+    """DualCache keeps every position outside the block at the K/V of the last refresh
+    (ccyt168.com Fast-dLLM article, section 1.1; techwalker.com explainer, "Core
+    innovation").  With the output projection of every layer but l* zeroed, layers 0..l*
+    see each position's own token alone, so the cached K/V at l* equal fresh ones and the
+    later layers never use theirs: every cached step of every block must give the no-cache
+    full forward's logits.  fp32 at 1e-4 against the oracle's full forward (not its cached
+    step), teacher-forced, one token per step (tau > 1)."""
+    wl = replace(synth.WORKLOADS["tiny_dual"], threshold=1.5)
+    wl = replace(wl, model=replace(wl.model, n_kv_heads=Hkv))
+    m = wl.model
+    W = synth.make_weights(wl)
+    for l in range(m.n_layers):
+        if l != l_star:
+            W[f"w_o.{l}"] = np.zeros_like(W[f"w_o.{l}"])
+    M = om.OracleModel(wl, weights=W)
+    prompt = synth.make_prompt(wl)
+    osess = OSession(M, prompt, wl.gen_len, wl.block_len, wl.threshold, "dual")
+    gsess = Session(Model.from_host(lib, m, W), prompt, wl.gen_len, wl.block_len,
+                    wl.threshold, "dual")
+    n = 0
+    for b in range(osess.n_blocks):
+        osess.refresh()
+        if b == 0:
+            gsess.prefill()
+        else:
+            gsess.refresh(b)
+        while not osess.block_done(b):
+            s0, s1 = osess.block_span(b)
+            gsess.tokens.copy_(torch.from_numpy(osess.tokens.astype(np.int32)))
+            _, ref = om.full_forward(M, osess.tokens, logit_rows=slice(s0, s1))
+            g = gsess.step(b)
+            torch.cuda.synchronize()
+            got = g["logits"].cpu().numpy().reshape(ref.shape).astype(np.float64)
+            assert rel_inf(got, ref) < 1e-4, f"block {b} step {n}"
+            osess.step(b)
+            n += 1
+    assert n == wl.gen_len
+
+
 @pytest.mark.parametrize("kind", ["fp32", "bf16"])
 def test_teacher_forced_largest_block(lib, kind):
     """Blocks of 64 positions, the largest the library takes (one wave ballot per block):
