@@ -1341,28 +1341,18 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
   // while the 128-row tiles read it twice; worth it once it fills a round of CUs
   const bool big_mid = M >= 256 && M < 512 && big_tiles >= 256;
   // Non-residual GEMMs whose ragged last round of large tiles is made of whole column
-  // tiles: the leading columns run as whole tiles, and the trailing ones either as
-  // 128x128 tiles when those fill a round of CUs (e.g. the 2024-row QKV: 256 large tiles,
-  // then 16 x 2 columns x 16 rows of small tiles), or split over K into about one round of
-  // large-tile pieces (partials, reduce_epilogue).
+  // tiles: the leading columns run as whole tiles, and the trailing ones either split over
+  // K into about one round of large-tile pieces (partials, reduce_epilogue; e.g. the
+  // 2024-row QKV: 256 large tiles, then 2 x 128 pieces), or, where a round holds fewer
+  // than two pieces per tail tile, as 128x128 tiles when those fill a round of CUs.  (The
+  // 2024-row QKV took 30.19 ms per 8B refresh with its tail as 512 small tiles, 29.98 ms
+  // split over K.)
   if (K % TB_K == 0 && M >= 512 && epi != EPI_RESID) {
     const int P = num_cus();
     const int ntn = (Nv + BG_T - 1) / BG_T, ntm = (M + BG_T - 1) / BG_T;
     const int tail = (ntn * ntm) % P;
     const int S = tail ? std::min(P / tail, K / TB_K) : 0;
     // the reduction reads float4 columns and, for QKV, whole head slots
-    if (ntn * ntm > P && tail % ntm == 0 && 4 * tail >= P) {
-      // the tail's columns as 128x128 tiles (4 per large tile) fill a round of CUs: run
-      // them on the tiled kernel, whole K, epilogue in place (no partials)
-      p.kind = GEMM_BIG;
-      p.ntn = ntn;
-      p.ntm = ntm;
-      p.ndp = ntn - tail / ntm;
-      p.tail_tiled = true;
-      p.kchunk = K;
-      p.splits = 1;
-      return p;
-    }
     if (ntn * ntm > P && tail % ntm == 0 && S >= 2 && Nv % 4 == 0 &&
         (epi != EPI_QKV || Nv % 128 == 0)) {
       p.kind = GEMM_BIG;
@@ -1375,6 +1365,18 @@ GemmPlan gemm_plan(int dtype, int M, int Nv, int K, int epi) {
       p.part_floats = (size_t)p.splits * M * (Nv - p.ndp * BG_T);
       p.deferred = true;
       p.reduce = true;
+      return p;
+    }
+    if (ntn * ntm > P && tail % ntm == 0 && 4 * tail >= P) {
+      // the tail's columns as 128x128 tiles (4 per large tile) fill a round of CUs: run
+      // them on the tiled kernel, whole K, epilogue in place (no partials)
+      p.kind = GEMM_BIG;
+      p.ntn = ntn;
+      p.ntm = ntm;
+      p.ndp = ntn - tail / ntm;
+      p.tail_tiled = true;
+      p.kchunk = K;
+      p.splits = 1;
       return p;
     }
   }

@@ -288,8 +288,11 @@ GEMM_CASES = [
     ("big_m1064_two_row_tiles", 1064, 768, 1024, "bf16"),
     # 72 x 4 large tiles: 256 whole tiles, then 8 column tiles x 4 row tiles in 8 K pieces
     ("big_m800_whole_and_split_tail", 800, 18400, 512, "bf16"),
-    # 80 x 4 large tiles: 256 whole, then 16 x 8 column tiles of 128 x 128
-    ("big_m800_whole_and_tiled_tail", 800, 20400, 512, "bf16"),
+    # 80 x 4 large tiles: 256 whole, then 16 x 4 column tiles in 4 K pieces
+    ("big_m800_whole_and_split_tail_4", 800, 20400, 512, "bf16"),
+    # 104 x 4 large tiles: 256 whole, then 40 x 4 (too many for two K pieces each in a
+    # round) as 80 x 7 tiles of 128 x 128
+    ("big_m800_whole_and_tiled_tail", 800, 26496, 512, "bf16"),
     ("f32_small", 20, 200, 64, "f32"),
 ]
 
